@@ -1,0 +1,224 @@
+"""Benchmark: one MuonClip layer step on one MI355X.
+
+A step is the whole path on the MuonClip attention layer (hidden 7168,
+64 heads x 128, batch 4 x seq 4096, bf16): the per-head causal max-logit
+statistic on the forward's Q and K, the Muon step (momentum + Nesterov +
+Frobenius pass, 5 quintic Newton-Schulz iterations as bf16 MFMA GEMMs,
+scaled and decayed parameter write) on W_q, W_k, W_v [8192 x 7168] and
+W_o [7168 x 8192], then the per-head W_q / W_k rescale at tau = 100.
+
+Inputs are seeded and synthetic and resident in HBM before timing.  Per-kernel
+times come from HIP events recorded by the library around each launch on the
+benchmark stream.  The CPU baseline times the fp64 oracle on a bounded sample
+of the same workload and extrapolates to one step.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=5000)
+    return ap.parse_args()
+
+
+def ns_flops(m, n):
+    """Algorithmic flops of one Newton-Schulz iteration on a wide m x n matrix
+    with the symmetric products counted once: X X^T (upper triangle incl.
+    diagonal: m(m+1)/2 dots of length n), A A^T (m(m+1)/2 dots of length m),
+    B X (m n dots of length m)."""
+    return {"ns_syrk_xxt": m * (m + 1) * n, "ns_syrk_poly": m * m * (m + 1), "ns_gemm_bx": 2 * m * m * n}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import matrix_orthogonalizing_optimizer_muon_amd as mm
+    from synthetic import generators as gen
+
+    dev = torch.device("cuda:0")
+    wl = gen.workload(5)
+    ex = wl.extra
+    B, T, H, D, dm = ex["batch"], ex["seq"], ex["heads"], ex["d_head"], ex["d_model"]
+    seed = args.seed
+
+    # ---------------- inputs (not timed)
+    qk = gen.qk_inputs_torch(seed, B, T, H, D, dm, ex["n_designated"], ex["targets"], dev)
+    Wqkv = gen.bulk_normal_torch((3, H * D, dm), wl.weight_std, seed + 10, dev, torch.bfloat16)
+    Wqkv[0].copy_(qk["Wq"])
+    Wqkv[1].copy_(qk["Wk"])
+    Wo = gen.bulk_normal_torch((1, dm, H * D), wl.weight_std, seed + 11, dev, torch.bfloat16)
+    Gqkv = gen.bulk_normal_torch((3, H * D, dm), 1.0, seed + 12, dev, torch.bfloat16)
+    Go = gen.bulk_normal_torch((1, dm, H * D), 1.0, seed + 13, dev, torch.bfloat16)
+    Mqkv = gen.bulk_normal_torch((3, H * D, dm), 0.5, seed + 14, dev, torch.float32)
+    Mo = gen.bulk_normal_torch((1, dm, H * D), 0.5, seed + 15, dev, torch.float32)
+    # the forward's projections on the pre-update weights (model work, not timed)
+    Q = (qk["X"] @ Wqkv[0].t()).view(B, T, H, D).contiguous()
+    K = (qk["X"] @ Wqkv[1].t()).view(B, T, H, D).contiguous()
+    del qk
+    groups = [(Wqkv, Gqkv, Mqkv), (Wo, Go, Mo)]
+    hp = mm.HParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay,
+                    nesterov=True, ns_steps=wl.ns_steps, ns_coeffs=wl.ns_coeffs,
+                    ns_eps=wl.ns_eps, rms_target=wl.rms_target)
+    ws = torch.empty(mm.workspace_size(groups), dtype=torch.uint8, device=dev)
+    s_max = torch.empty(H, dtype=torch.float32, device=dev)
+    clipped = torch.empty(H, dtype=torch.int32, device=dev)
+    rm_ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        mm.qkclip_rowmax(Q, K, 1.0 / math.sqrt(D), True, out=s_max, workspace=rm_ws)
+        mm.muon_step(groups, hp, workspace=ws)
+        mm.qkclip_rescale(Wqkv[0], Wqkv[1], s_max, D, ex["tau"], ex["alpha"], clipped=clipped)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---------------- timed region
+    mm.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = mm.profile_collect()
+    mm.profile_enable(False)
+
+    n_clipped = int((clipped == 1).sum())
+    ms_per_step = 1e3 * elapsed / args.steps
+    steps_per_s = args.steps / elapsed
+
+    # ---------------- Newton-Schulz throughput and the dominant kernel's roofline
+    m, n = 7168, 8192                      # every matrix is 7168 x 8192 once oriented wide
+    n_mats = 4
+    per_iter = ns_flops(m, n)
+    ns_flop_step = n_mats * wl.ns_steps * sum(per_iter.values())
+    ns_ms_step = sum(prof[k][0] for k in per_iter) / args.steps
+    ns_tflops = ns_flop_step / (ns_ms_step * 1e-3) / 1e12
+    kernels = {k: {"total_ms": round(v[0], 4), "launches": v[1],
+                   "avg_us": round(1e3 * v[0] / v[1], 2) if v[1] else None}
+               for k, v in prof.items() if v[1]}
+    dom = max(per_iter, key=lambda k: prof[k][0])
+    dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
+    dom_flop = n_mats * per_iter[dom]
+    achieved = dom_flop / dom_avg_s / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    # HBM passes: algorithmic bytes per launch over their event time
+    elem = 4 * m * n
+    hbm = {}
+    mom_bytes = elem * (2 + 4 + 4 + 2 + 2)      # G bf16, M r/w fp32, X0 and X0^T bf16
+    upd_bytes = elem * (2 + 2 + 2)              # O bf16, W bf16 r/w
+    for k, by in (("momentum_norm", mom_bytes), ("param_update", upd_bytes)):
+        if prof[k][1]:
+            t = prof[k][0] / prof[k][1] * 1e-3
+            hbm[k] = {"GBs": round(by / t / 1e9, 1), "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+                      "bytes": by}
+    if prof["qk_rowmax"][1]:
+        qk_flop = 2 * D * B * H * T * (T + 1) / 2
+        t = prof["qk_rowmax"][0] / prof["qk_rowmax"][1] * 1e-3
+        kernels["qk_rowmax"]["tflops"] = round(qk_flop / t / 1e12, 1)
+        kernels["qk_rowmax"]["frac_mfma_peak"] = round(qk_flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+
+    out = {
+        "metric": "Muon steps/s + Newton–Schulz TFLOP/s (% bf16 MFMA peak), 1 MI355X",
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "MuonClip layer: hidden 7168, 64 heads x 128, batch 4 x seq 4096; "
+                               "Muon step on W_q, W_k, W_v [8192x7168] and W_o [7168x8192]",
+                   "ns_steps": wl.ns_steps, "tau": ex["tau"], "parallelism": "single GPU"},
+        "ns_tflops": round(ns_tflops, 1),
+        "ns_frac_mfma_peak": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "ns_ms_per_step": round(ns_ms_step, 3),
+        "roofline": roofline,
+        "hbm_passes": hbm,
+        "kernels": kernels,
+        "heads_clipped_per_step": n_clipped,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, m, n, n_mats, B, T, H, D):
+    """Time the fp64 oracle on a bounded sample and extrapolate to one step:
+    one Newton-Schulz iteration, the momentum and update of one 7168 x 8192
+    matrix, and the causal logit maximum of one (batch row, head) pair."""
+    import numpy as np
+
+    from oracle import muon_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    g = np.random.default_rng(1)
+    X = g.standard_normal((m, n))
+    X /= np.linalg.norm(X)
+    t0 = time.perf_counter()
+    O.newton_schulz_iterate(X, 1, *wl.ns_coeffs)
+    t_iter = time.perf_counter() - t0
+    W = g.standard_normal((m, n)) * 0.02
+    M = g.standard_normal((m, n)) * 0.5
+    G = g.standard_normal((m, n))
+    t0 = time.perf_counter()
+    Mn = O.momentum_update(M, G, wl.momentum)
+    U = O.nesterov_lookahead(Mn, G, wl.momentum, True)
+    O.frobenius_normalize(U, wl.ns_eps)
+    O.param_update(W, U, wl.lr, wl.weight_decay, 18.1)
+    t_elem = time.perf_counter() - t0
+    Qs = g.standard_normal((1, T, 1, D))
+    Ks = g.standard_normal((1, T, 1, D))
+    t0 = time.perf_counter()
+    O.smax_per_head(Qs, Ks, 1 / math.sqrt(D), True)
+    t_pair = time.perf_counter() - t0
+    step_s = n_mats * (wl.ns_steps * t_iter + t_elem) + B * H * t_pair
+    return {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle: 1 Newton-Schulz iteration ({t_iter:.2f} s) and the "
+                       f"momentum/normalise/update pass ({t_elem:.2f} s) of one 7168x8192 matrix, "
+                       f"S_max of one (batch row, head) pair ({t_pair:.2f} s); extrapolated to "
+                       f"{n_mats} matrices x {wl.ns_steps} iterations + {B * H} pairs"),
+            "seconds_per_step": round(step_s, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * muon.h — C ABI of libmuon: the Muon optimizer step and MuonClip's QK-Clip
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MC] "MuonClip" — 02 Muon from first principles; 03 Making Muon scale;
+ *        05 QK-Clip; 06 Multi-head latent attention changes the surgery;
+ *        07 One complete training step.
+ *   [MM] "Muon and MuonClip: orthogonalised updates for LLM training" —
+ *        section 2: "Newton-Schulz: an odd polynomial on singular values",
+ *        "The Muon optimizer", "The exploding-logit problem",
+ *        "MuonClip: QK-clip, per head, adapted to MLA".
+ *   [MS] "About Muon: Muon At Scale" — "Why Not Bernstein's Multiplier?",
+ *        "When Softmax Collapses".
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers unless stated otherwise; the structs
+ *     passed by pointer (muon_group_t arrays, muon_hparams_t) are HOST memory
+ *     read during the call only.
+ *   - Matrices are row-major [rows][cols] with rows = fan-out (the layout of
+ *     a Linear weight).  A group is `batch` same-shape matrices, matrix b
+ *     starting `batch_stride` elements after matrix b-1.
+ *   - bf16 is IEEE binary32's upper half, passed as uint16_t storage.
+ *   - The caller owns every buffer.  The library never allocates device
+ *     memory.  Scratch space is the caller's `workspace`, sized by the
+ *     matching *_workspace_size query; its contents are undefined between
+ *     calls except where a layout query below says otherwise.
+ *   - Every call is asynchronous on `stream` and never synchronises it.
+ *     Argument errors are detected on the host before any launch and are
+ *     returned synchronously; nothing is launched then.  Launch failures
+ *     return MUON_ERR_HIP.  Data-dependent conditions (non-finite values)
+ *     never raise errors: NaN/Inf in gradients propagate into the outputs;
+ *     a non-finite S_max is reported through the `clipped` flags.
+ *   - Calls on different streams are safe if their workspaces and outputs
+ *     do not overlap.  The optional profiler (muon_profile_*) is process-wide
+ *     and not thread-safe.
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum   */
+  MUON_ERR_UNSUPPORTED = 2, /* valid but not built (e.g. d_head not 64/128/256) */
+  MUON_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required  */
+  MUON_ERR_HIP = 4          /* a HIP launch or runtime call failed          */
+} muon_status_t;
+
+typedef enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 } muon_dtype_t;
+
+/* Multiplier on the orthogonalised update ([MC] 03; [MS] "Why Not Bernstein's
+ * Multiplier?"):
+ *   MOONLIGHT: rms_target * sqrt(max(rows, cols))  (entry RMS ~ rms_target)
+ *   SPECTRAL:  sqrt(rows / cols)                   (sqrt(fan-out / fan-in))
+ *   NONE:      1                                                            */
+typedef enum {
+  MUON_SCALE_MOONLIGHT = 0,
+  MUON_SCALE_SPECTRAL = 1,
+  MUON_SCALE_NONE = 2
+} muon_scale_mode_t;
+
+/* Hyper-parameters of one Muon step.
+ *   momentum:  M_t = momentum * M_{t-1} + G_t  ([MC] 02; sum form)
+ *   nesterov:  nonzero -> Newton-Schulz input U = G_t + momentum * M_t,
+ *              zero    -> U = M_t
+ *   ns_*:      ns_steps iterations of X <- a X + (b A + c A A) X, A = X X^T,
+ *              on X_0 = U / (||U||_F + ns_eps) in the wide orientation
+ *              (transpose when rows > cols)  ([MM] Newton-Schulz subsection)
+ *   update:    W <- (1 - lr * weight_decay) W - lr * scale * O  ([MC] 03),
+ *              in fp32, rounded once (nearest-even) to the parameter dtype. */
+typedef struct {
+  float lr;
+  float momentum;
+  float weight_decay;
+  int32_t nesterov;
+  int32_t ns_steps; /* 0..64 */
+  float ns_a, ns_b, ns_c;
+  float ns_eps;
+  int32_t scale_mode; /* muon_scale_mode_t */
+  float rms_target;   /* used by MUON_SCALE_MOONLIGHT */
+} muon_hparams_t;
+
+/* One group of same-shape matrices.  param/grad: param dtype; momentum: fp32;
+ * all three [batch][rows][cols] with the same batch_stride (in elements,
+ * >= rows*cols).  param and momentum are updated in place; grad is read. */
+typedef struct {
+  void* param;
+  const void* grad;
+  float* momentum;
+  int32_t batch;
+  int32_t rows;
+  int32_t cols;
+  int32_t reserved; /* must be 0 */
+  int64_t batch_stride;
+} muon_group_t;
+
+#define MUON_MAX_GROUPS 16
+
+/* ---------------------------------------------------------------- muon_step
+ * One full Muon step ([MC] 07 pseudocode order) over n_groups groups sharing
+ * one parameter dtype: momentum update and Nesterov lookahead fused with the
+ * Frobenius partial sums in one pass; Newton-Schulz on bf16 MFMA with fp32
+ * accumulation, every same-shape matrix of every group batched into one
+ * launch per stage; then the scaled, decayed parameter write.
+ *   groups:          host array of n_groups descriptors (1..MUON_MAX_GROUPS)
+ *   param_dtype:     MUON_DTYPE_F32 or MUON_DTYPE_BF16 (grads share it)
+ *   hp:              host pointer, see muon_hparams_t
+ *   workspace:       device scratch of >= muon_step_workspace_size(...) bytes,
+ *                    256-byte aligned
+ * Returns MUON_OK or an error code (see conventions).                       */
+size_t muon_step_workspace_size(const muon_group_t* groups, int n_groups);
+int muon_step(const muon_group_t* groups, int n_groups, int param_dtype,
+              const muon_hparams_t* hp, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/* Where muon_step leaves its intermediate results, as byte offsets into the
+ * workspace of the last call with the same groups (valid until the workspace
+ * is reused):
+ *   o_offset:       bf16 Newton-Schulz output O of group g, in the group's
+ *                   own layout: matrix b, element (i, j) at
+ *                   o_offset + 2 * (b * o_batch_stride + i * o_ld + j)
+ *   inv_norm_offset: fp32 [batch] values 1 / (||U_b||_F + ns_eps)
+ *   x0_offset:       bf16 U (unnormalised, rounded once) in the wide
+ *                   orientation: (i, j) of the m x n wide view at
+ *                   x0_offset + 2 * (b * x0_batch_stride + i * x0_ld + j);
+ *                   only after a call with ns_steps == 1 (later iterations
+ *                   reuse that buffer)                                      */
+typedef struct {
+  size_t o_offset;
+  int64_t o_batch_stride;
+  int64_t o_ld;
+  size_t inv_norm_offset;
+  size_t x0_offset;
+  int64_t x0_batch_stride;
+  int64_t x0_ld;
+} muon_ws_layout_t;
+int muon_step_workspace_layout(const muon_group_t* groups, int n_groups, int g,
+                               int ns_steps, muon_ws_layout_t* out);
+
+/* ---------------------------------------------------------- ns_orthogonalize
+ * Newton-Schulz alone ([MM] Newton-Schulz subsection): for each of `batch`
+ * matrices in (dtype in_dtype, [rows][cols], batch_stride elements apart),
+ * out = NS_steps(in / (||in||_F + eps)) written as bf16 into `out`, dense
+ * [batch][rows][cols].  Same arithmetic and kernels as muon_step.          */
+size_t ns_workspace_size(int batch, int rows, int cols);
+int ns_orthogonalize(const void* in, int in_dtype, uint16_t* out, int batch,
+                     int rows, int cols, int64_t batch_stride, int steps,
+                     float a, float b, float c, float eps, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------- qkclip_rowmax
+ * Per-head maximum pre-softmax logit ([MM] "The exploding-logit problem";
+ * [MC] 05 per-head signal):
+ *   s_max[h] = logit_scale * max over b < B, i < T, j < T (j <= i if causal)
+ *              of sum_t Q[b,i,h,t] * K[b,j,h,t]
+ * Q, K: bf16 [B][T][H][d_head] (the forward's projections, row-major).
+ * logit_scale is normally 1/sqrt(d_head).  d_head must be 64, 128 or 256.
+ * s_max: fp32 [H] device output.  A NaN anywhere in a head's logits makes
+ * s_max[h] NaN.  Products are bf16 x bf16 exact, accumulated in fp32.
+ * workspace: >= qkclip_rowmax_workspace_size(B, T, H) bytes.               */
+size_t qkclip_rowmax_workspace_size(int B, int T, int H);
+int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H,
+                  int d_head, float logit_scale, int causal, float* s_max,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ qkclip_rescale
+ * Balanced MHA QK-Clip ([MC] 05 balanced rescale; [MS] "When Softmax
+ * Collapses"): for each head h with finite s_max[h] > tau,
+ *   gamma = tau / s_max[h];  rows [h*d_head, (h+1)*d_head) of Wq *= gamma^alpha,
+ *   the same rows of Wk *= gamma^(1-alpha)  (fp32 product, one rounding).
+ * Heads with s_max <= tau are untouched; NaN/Inf s_max leaves the head
+ * untouched.  Wq, Wk: [H*d_head][d_model] of `dtype`, updated in place.
+ * s_max: fp32 [H] device input (e.g. from qkclip_rowmax).  clipped: optional
+ * int32 [H] device output, 1 clipped, 0 untouched, -1 non-finite s_max.
+ * The momentum buffers are not touched ([MC] 07).                          */
+int qkclip_rescale(void* Wq, void* Wk, int dtype, int H, int d_head,
+                   int d_model, const float* s_max, float tau, float alpha,
+                   int32_t* clipped, hipStream_t stream);
+
+/* -------------------------------------------------------------- diagnostics */
+const char* muon_status_string(int status);
+
+/* Optional per-kernel timing with HIP events recorded around every launch
+ * the library makes on the caller's stream.  muon_profile_enable(1) clears
+ * and starts recording; muon_profile_collect() waits for the recorded events,
+ * fills up to n_kinds entries of total milliseconds and launch counts per
+ * kernel kind (index = kind id) and returns the number of kinds.
+ * muon_kernel_kind_name(k) names kind k.  Process-wide, not thread-safe.   */
+int muon_profile_enable(int on);
+int muon_profile_collect(double* total_ms, int64_t* launches, int n_kinds);
+const char* muon_kernel_kind_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUON_H */

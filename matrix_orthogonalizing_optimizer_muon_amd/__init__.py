@@ -1,0 +1,330 @@
+"""Muon optimizer step and MuonClip QK-Clip on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libmuon.so (C ABI in include/muon.h).  Every step of
+the computation runs in the library's HIP kernels; this module only checks
+tensor arguments, passes raw device pointers and torch's current HIP stream,
+and allocates workspaces with torch.  There is no fallback: if the library is
+missing or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmuon.so")
+
+MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_ERR_HIP = range(5)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+SCALE_MODES = {"moonlight": 0, "spectral": 1, "none": 2}
+MAX_GROUPS = 16
+KERNEL_KINDS = 9
+
+# ---------------------------------------------------------------------------
+# C structs
+# ---------------------------------------------------------------------------
+
+
+class _HParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("nesterov", ctypes.c_int32),
+                ("ns_steps", ctypes.c_int32), ("ns_a", ctypes.c_float),
+                ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
+                ("ns_eps", ctypes.c_float), ("scale_mode", ctypes.c_int32),
+                ("rms_target", ctypes.c_float)]
+
+
+class _Group(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("momentum", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("batch_stride", ctypes.c_int64)]
+
+
+class _WsLayout(ctypes.Structure):
+    _fields_ = [("o_offset", ctypes.c_size_t), ("o_batch_stride", ctypes.c_int64),
+                ("o_ld", ctypes.c_int64), ("inv_norm_offset", ctypes.c_size_t),
+                ("x0_offset", ctypes.c_size_t), ("x0_batch_stride", ctypes.c_int64),
+                ("x0_ld", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmuon.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i64, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    G = ctypes.POINTER(_Group)
+    lib.muon_step_workspace_size.argtypes = [G, i32]
+    lib.muon_step_workspace_size.restype = sz
+    lib.muon_step.argtypes = [G, i32, i32, ctypes.POINTER(_HParams), vp, sz, vp]
+    lib.muon_step.restype = i32
+    lib.muon_step_workspace_layout.argtypes = [G, i32, i32, i32, ctypes.POINTER(_WsLayout)]
+    lib.muon_step_workspace_layout.restype = i32
+    lib.ns_workspace_size.argtypes = [i32, i32, i32]
+    lib.ns_workspace_size.restype = sz
+    lib.ns_orthogonalize.argtypes = [vp, i32, vp, i32, i32, i32, i64, i32, f32, f32, f32, f32, vp, sz, vp]
+    lib.ns_orthogonalize.restype = i32
+    lib.qkclip_rowmax_workspace_size.argtypes = [i32, i32, i32]
+    lib.qkclip_rowmax_workspace_size.restype = sz
+    lib.qkclip_rowmax.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, sz, vp]
+    lib.qkclip_rowmax.restype = i32
+    lib.qkclip_rescale.argtypes = [vp, vp, i32, i32, i32, i32, vp, f32, f32, vp, vp]
+    lib.qkclip_rescale.restype = i32
+    lib.muon_status_string.argtypes = [i32]
+    lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_profile_enable.argtypes = [i32]
+    lib.muon_profile_enable.restype = i32
+    lib.muon_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32]
+    lib.muon_profile_collect.restype = i32
+    lib.muon_kernel_kind_name.argtypes = [i32]
+    lib.muon_kernel_kind_name.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load_library()
+        super().__init__(f"{where}: {lib.muon_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != MUON_OK:
+        raise MuonError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# helpers (torch is used for device memory and the stream handle only)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _as3d(t):
+    """View a [rows, cols] or [batch, rows, cols] tensor as (batch, rows, cols,
+    batch_stride); rows must be contiguous."""
+    if t.dim() == 2:
+        if not t.is_contiguous():
+            raise ValueError("matrices must be row-major contiguous")
+        return 1, t.shape[0], t.shape[1], t.shape[0] * t.shape[1]
+    if t.dim() == 3:
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2] or t.stride(0) < t.shape[1] * t.shape[2]:
+            raise ValueError("each matrix must be row-major contiguous")
+        return t.shape[0], t.shape[1], t.shape[2], t.stride(0)
+    raise ValueError("expected a 2-D or 3-D tensor")
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    # 256-byte alignment: torch's caching allocator returns >= 512-byte aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class HParams:
+    """Muon hyper-parameters (defaults: the pages' common settings)."""
+    lr: float = 0.02
+    momentum: float = 0.95
+    weight_decay: float = 0.1
+    nesterov: bool = True
+    ns_steps: int = 5
+    ns_coeffs: tuple = (3.4445, -4.7750, 2.0315)
+    ns_eps: float = 1e-7
+    scale_mode: str = "moonlight"
+    rms_target: float = 0.2
+
+    def to_c(self) -> _HParams:
+        a, b, c = self.ns_coeffs
+        return _HParams(self.lr, self.momentum, self.weight_decay, int(bool(self.nesterov)),
+                        int(self.ns_steps), a, b, c, self.ns_eps, SCALE_MODES[self.scale_mode],
+                        self.rms_target)
+
+
+def _groups_c(groups):
+    if not 1 <= len(groups) <= MAX_GROUPS:
+        raise ValueError(f"1..{MAX_GROUPS} groups per call")
+    arr = (_Group * len(groups))()
+    dtype = None
+    for k, (p, g, m) in enumerate(groups):
+        _need_cuda(p, g, m)
+        torch = _torch()
+        if p.shape != g.shape or p.shape != m.shape:
+            raise ValueError("param, grad and momentum must share a shape")
+        if p.dtype != g.dtype:
+            raise TypeError("grad must have the param dtype")
+        if m.dtype != torch.float32:
+            raise TypeError("momentum must be float32")
+        dc = _dtype_code(p)
+        if dtype is None:
+            dtype = dc
+        elif dc != dtype:
+            raise TypeError("all groups of one call share a param dtype")
+        b, r, c, st = _as3d(p)
+        if _as3d(g)[3] != st or _as3d(m)[3] != st:
+            raise ValueError("param, grad and momentum must share the batch stride")
+        arr[k] = _Group(p.data_ptr(), g.data_ptr(), m.data_ptr(), b, r, c, 0, st)
+    return arr, dtype
+
+
+def workspace_size(groups) -> int:
+    lib = load_library()
+    arr, _ = _groups_c(groups)
+    return int(lib.muon_step_workspace_size(arr, len(groups)))
+
+
+def muon_step(groups, hp: HParams | None = None, workspace=None):
+    """One Muon step, in place, over a list of (param, grad, momentum) groups
+    ([batch, rows, cols] or [rows, cols] tensors).  Returns the workspace
+    tensor (reusable for the next call with the same groups)."""
+    lib = load_library()
+    hp = hp or HParams()
+    arr, dtype = _groups_c(groups)
+    need = int(lib.muon_step_workspace_size(arr, len(groups)))
+    if workspace is None:
+        workspace = _workspace(need, groups[0][0].device)
+    h = hp.to_c()
+    _check(lib.muon_step(arr, len(groups), dtype, ctypes.byref(h), workspace.data_ptr(),
+                         workspace.numel(), _stream()), "muon_step")
+    return workspace
+
+
+def workspace_views(groups, g: int, workspace, ns_steps: int = 5):
+    """(O, inv_norm, X0) tensors viewing the workspace after muon_step:
+    O [batch, rows, cols] bf16 (group layout), inv_norm [batch] fp32 and
+    X0 [batch, m, n] bf16 (wide orientation, unnormalised)."""
+    torch = _torch()
+    lib = load_library()
+    arr, _ = _groups_c(groups)
+    lay = _WsLayout()
+    _check(lib.muon_step_workspace_layout(arr, len(groups), g, ns_steps, ctypes.byref(lay)),
+           "muon_step_workspace_layout")
+    b, r, c, _ = _as3d(groups[g][0])
+    m, n = min(r, c), max(r, c)
+    bf = workspace.view(torch.bfloat16) if workspace.numel() % 2 == 0 else None
+    o = torch.as_strided(bf, (b, r, c), (lay.o_batch_stride, lay.o_ld, 1), lay.o_offset // 2)
+    inv = torch.as_strided(workspace.view(torch.float32), (b,), (1,), lay.inv_norm_offset // 4)
+    x0 = torch.as_strided(bf, (b, m, n), (lay.x0_batch_stride, lay.x0_ld, 1), lay.x0_offset // 2)
+    return o, inv, x0
+
+
+def ns_orthogonalize(x, steps: int = 5, coeffs=(3.4445, -4.7750, 2.0315), eps: float = 1e-7,
+                     out=None, workspace=None):
+    """Newton-Schulz on each matrix of x ([rows, cols] or [batch, rows, cols],
+    float32 or bfloat16); returns bf16 of the same shape."""
+    torch = _torch()
+    lib = load_library()
+    _need_cuda(x)
+    b, r, c, st = _as3d(x)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of x's shape")
+    need = int(lib.ns_workspace_size(b, r, c))
+    if workspace is None:
+        workspace = _workspace(need, x.device)
+    a_, b_, c_ = coeffs
+    _check(lib.ns_orthogonalize(x.data_ptr(), _dtype_code(x), out.data_ptr(), b, r, c, st, steps,
+                                a_, b_, c_, eps, workspace.data_ptr(), workspace.numel(), _stream()),
+           "ns_orthogonalize")
+    return out
+
+
+def qkclip_rowmax(Q, K, logit_scale: float | None = None, causal: bool = True, out=None,
+                  workspace=None):
+    """Per-head maximum logit of bf16 Q, K [B, T, H, d_head]; returns fp32 [H]."""
+    torch = _torch()
+    lib = load_library()
+    _need_cuda(Q, K)
+    if Q.dtype != torch.bfloat16 or K.dtype != torch.bfloat16:
+        raise TypeError("Q and K must be bfloat16")
+    if Q.dim() != 4 or Q.shape != K.shape or not Q.is_contiguous() or not K.is_contiguous():
+        raise ValueError("Q and K must be contiguous [B, T, H, d_head] tensors of one shape")
+    B, T, H, D = Q.shape
+    if logit_scale is None:
+        logit_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty(H, dtype=torch.float32, device=Q.device)
+    need = int(lib.qkclip_rowmax_workspace_size(B, T, H))
+    if workspace is None:
+        workspace = _workspace(need, Q.device)
+    _check(lib.qkclip_rowmax(Q.data_ptr(), K.data_ptr(), B, T, H, D, logit_scale, int(bool(causal)),
+                             out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
+           "qkclip_rowmax")
+    return out
+
+
+def qkclip_rescale(Wq, Wk, s_max, d_head: int, tau: float = 100.0, alpha: float = 0.5,
+                   clipped=None):
+    """In-place per-head rescale of Wq, Wk [H*d_head, d_model]; returns the
+    int32 [H] flags (1 clipped, 0 untouched, -1 non-finite S_max)."""
+    torch = _torch()
+    lib = load_library()
+    _need_cuda(Wq, Wk, s_max)
+    if Wq.shape != Wk.shape or Wq.dim() != 2 or not Wq.is_contiguous() or not Wk.is_contiguous():
+        raise ValueError("Wq and Wk must be contiguous 2-D tensors of one shape")
+    if Wq.dtype != Wk.dtype:
+        raise TypeError("Wq and Wk must share a dtype")
+    rows, d_model = Wq.shape
+    if rows % d_head:
+        raise ValueError("rows of Wq must be a multiple of d_head")
+    H = rows // d_head
+    if s_max.dtype != torch.float32 or s_max.numel() != H:
+        raise ValueError("s_max must be float32 [H]")
+    if clipped is None:
+        clipped = torch.empty(H, dtype=torch.int32, device=Wq.device)
+    _check(lib.qkclip_rescale(Wq.data_ptr(), Wk.data_ptr(), _dtype_code(Wq), H, d_head, d_model,
+                              s_max.data_ptr(), tau, alpha, clipped.data_ptr(), _stream()),
+           "qkclip_rescale")
+    return clipped
+
+
+def profile_enable(on: bool = True):
+    load_library().muon_profile_enable(int(bool(on)))
+
+
+def profile_collect() -> dict:
+    """{kernel kind name: (total_ms, launches)} for launches since profile_enable."""
+    lib = load_library()
+    ms = (ctypes.c_double * KERNEL_KINDS)()
+    cnt = (ctypes.c_int64 * KERNEL_KINDS)()
+    n = lib.muon_profile_collect(ms, cnt, KERNEL_KINDS)
+    if n < 0:
+        raise MuonError(-n, "muon_profile_collect")
+    return {lib.muon_kernel_kind_name(k).decode(): (ms[k], int(cnt[k])) for k in range(KERNEL_KINDS)}

@@ -1,0 +1,512 @@
+// libmuon C ABI: argument checks, workspace layout and launch sequencing for
+// the Muon step ("MuonClip", section 07 step order: momentum -> Newton-Schulz
+// -> scaled, decayed update), Newton-Schulz alone, and QK-Clip.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.hpp"
+
+namespace muon {
+
+// ----------------------------------------------------------------------------
+// optional event profiler
+// ----------------------------------------------------------------------------
+namespace {
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+int g_open_kind = -1;
+hipEvent_t g_open_start = nullptr;
+
+hipEvent_t pool_get() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void prof_begin(int kind, hipStream_t s) {
+  if (!g_prof_on) return;
+  g_open_kind = kind;
+  g_open_start = pool_get();
+  if (g_open_start) hipEventRecord(g_open_start, s);
+}
+
+void prof_end(int kind, hipStream_t s) {
+  if (!g_prof_on || !g_open_start || g_open_kind != kind) return;
+  hipEvent_t e = pool_get();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_prof.push_back({kind, g_open_start, e});
+  g_open_start = nullptr;
+  g_open_kind = -1;
+}
+
+// ----------------------------------------------------------------------------
+// workspace plan
+// ----------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+struct Plan {
+  int batch, rows, cols;
+  int64_t bstride;
+  bool tall;
+  int m, n;       // wide view, m <= n
+  int tile;       // Newton-Schulz GEMM tile edge
+  int mp, np;     // padded wide view (multiples of tile)
+  int rp, cp;     // padded original layout
+  int tiles_r, tiles_c, mom_tiles;
+  size_t off_X[2], off_Xt[2], off_A, off_B, off_part, off_inv;
+};
+
+Plan make_plan(int batch, int rows, int cols, int64_t bstride, size_t& cursor) {
+  Plan p{};
+  p.batch = batch;
+  p.rows = rows;
+  p.cols = cols;
+  p.bstride = bstride;
+  p.tall = rows > cols;
+  p.m = std::min(rows, cols);
+  p.n = std::max(rows, cols);
+  p.tile = (p.m >= 512) ? 256 : 128;
+  p.mp = round_up(p.m, p.tile);
+  p.np = round_up(p.n, p.tile);
+  p.rp = p.tall ? p.np : p.mp;
+  p.cp = p.tall ? p.mp : p.np;
+  p.tiles_r = p.rp / 64;
+  p.tiles_c = p.cp / 64;
+  p.mom_tiles = p.tiles_r * p.tiles_c;
+  const size_t xb = static_cast<size_t>(batch) * p.mp * p.np * sizeof(bf16_t);
+  const size_t ab = static_cast<size_t>(batch) * p.mp * p.mp * sizeof(bf16_t);
+  for (int k = 0; k < 2; ++k) {
+    p.off_X[k] = cursor;
+    cursor = align_up(cursor + xb);
+    p.off_Xt[k] = cursor;
+    cursor = align_up(cursor + xb);
+  }
+  p.off_A = cursor;
+  cursor = align_up(cursor + ab);
+  p.off_B = cursor;
+  cursor = align_up(cursor + ab);
+  p.off_part = cursor;
+  cursor = align_up(cursor + static_cast<size_t>(batch) * p.mom_tiles * sizeof(double));
+  p.off_inv = cursor;
+  cursor = align_up(cursor + static_cast<size_t>(batch) * sizeof(float));
+  return p;
+}
+
+bool dims_ok(int batch, int rows, int cols) {
+  if (batch < 1 || rows < 1 || cols < 1) return false;
+  // padded extents and per-matrix element counts stay inside int / the
+  // grid limits used by the kernels
+  if (rows > (1 << 20) || cols > (1 << 20)) return false;
+  const int64_t mx = std::max(rows, cols) + 256, mn = std::min(rows, cols) + 256;
+  if (mx * mn > (int64_t(1) << 31)) return false;
+  return true;
+}
+
+int check_groups(const muon_group_t* groups, int n_groups) {
+  if (!groups || n_groups < 1 || n_groups > MUON_MAX_GROUPS) return MUON_ERR_INVALID_ARG;
+  for (int g = 0; g < n_groups; ++g) {
+    const muon_group_t& G = groups[g];
+    if (!dims_ok(G.batch, G.rows, G.cols) || G.reserved != 0) return MUON_ERR_INVALID_ARG;
+    if (G.batch_stride < static_cast<int64_t>(G.rows) * G.cols) return MUON_ERR_INVALID_ARG;
+  }
+  return MUON_OK;
+}
+
+std::vector<Plan> plans_for(const muon_group_t* groups, int n_groups, size_t& total) {
+  std::vector<Plan> v;
+  size_t cursor = 0;
+  for (int g = 0; g < n_groups; ++g)
+    v.push_back(make_plan(groups[g].batch, groups[g].rows, groups[g].cols, groups[g].batch_stride, cursor));
+  total = cursor;
+  return v;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+#define MUON_LAUNCH(kind, stream, expr)            \
+  do {                                             \
+    prof_begin(kind, stream);                      \
+    hipError_t e_ = (expr);                        \
+    prof_end(kind, stream);                        \
+    if (e_ != hipSuccess) return MUON_ERR_HIP;     \
+  } while (0)
+
+// Input of one group to the fused momentum / normalisation pass.
+struct PrepIn {
+  const void* G;
+  float* M;
+};
+
+int launch_prep(const std::vector<Plan>& plans, const std::vector<PrepIn>& ins, int dtype, float mu,
+                int nesterov, void* ws, hipStream_t s) {
+  MomentumLaunch L{};
+  L.ngroups = static_cast<int>(plans.size());
+  L.mu = mu;
+  L.nesterov = nesterov;
+  int blocks = 0;
+  const size_t esz = dtype == MUON_DTYPE_BF16 ? 2 : 4;
+  for (size_t g = 0; g < plans.size(); ++g) {
+    const Plan& p = plans[g];
+    MomentumGroup& q = L.g[g];
+    q.G = ins[g].G;
+    q.M = ins[g].M;
+    q.bstride = p.bstride;
+    q.rows = p.rows;
+    q.cols = p.cols;
+    q.rp = p.rp;
+    q.cp = p.cp;
+    bf16_t* X0 = at<bf16_t>(ws, p.off_X[0]);
+    bf16_t* X0t = at<bf16_t>(ws, p.off_Xt[0]);
+    q.D1 = p.tall ? X0t : X0;
+    q.D2 = p.tall ? X0 : X0t;
+    q.d_stride = static_cast<int64_t>(p.rp) * p.cp;
+    q.partials = at<double>(ws, p.off_part);
+    q.tiles_r = p.tiles_r;
+    q.tiles_c = p.tiles_c;
+    q.tiles_per_mat = p.mom_tiles;
+    q.batch = p.batch;
+    q.vec = (p.cols % 4 == 0) && (p.bstride % 4 == 0) && aligned(q.G, 4 * esz) &&
+            (q.M == nullptr || aligned(q.M, 16));
+    L.prefix[g] = blocks;
+    blocks += p.batch * p.mom_tiles;
+  }
+  L.prefix[plans.size()] = blocks;
+  MUON_LAUNCH(KIND_MOMENTUM_NORM, s, launch_momentum_norm(L, dtype, blocks, s));
+  return MUON_OK;
+}
+
+int launch_finalize(const std::vector<Plan>& plans, float eps, void* ws, hipStream_t s) {
+  FinalizeLaunch F{};
+  F.ngroups = static_cast<int>(plans.size());
+  F.eps = eps;
+  int mats = 0;
+  for (size_t g = 0; g < plans.size(); ++g) {
+    F.prefix[g] = mats;
+    F.partials[g] = at<double>(ws, plans[g].off_part);
+    F.tiles_per_mat[g] = plans[g].mom_tiles;
+    F.inv_norm[g] = at<float>(ws, plans[g].off_inv);
+    mats += plans[g].batch;
+  }
+  F.prefix[plans.size()] = mats;
+  MUON_LAUNCH(KIND_NORM_FINALIZE, s, launch_norm_finalize(F, mats, s));
+  return MUON_OK;
+}
+
+// Final-step destination of a group: where the last X' is written.
+struct FinalOut {
+  bf16_t* ptr;      // null: keep in the workspace
+  int64_t stride;   // elements between matrices
+  int ld;           // leading dimension
+};
+
+enum Stage { STAGE_SYRK = 0, STAGE_POLY = 1, STAGE_BX = 2 };
+
+GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b, float c, void* ws,
+                   const FinalOut* fin) {
+  GemmProb q{};
+  const int cur = t & 1, nxt = cur ^ 1;
+  bf16_t* X = at<bf16_t>(ws, p.off_X[cur]);
+  bf16_t* Xt = at<bf16_t>(ws, p.off_Xt[cur]);
+  bf16_t* Xn = at<bf16_t>(ws, p.off_X[nxt]);
+  bf16_t* Xtn = at<bf16_t>(ws, p.off_Xt[nxt]);
+  bf16_t* A = at<bf16_t>(ws, p.off_A);
+  bf16_t* B = at<bf16_t>(ws, p.off_B);
+  const int64_t sx = static_cast<int64_t>(p.mp) * p.np, sa = static_cast<int64_t>(p.mp) * p.mp;
+  const int T = p.mp / p.tile;
+  q.alpha = at<float>(ws, p.off_inv);
+  q.ct_vec = 1;
+  if (stage == STAGE_SYRK) {
+    q.P = X; q.Q = X; q.sP = sx; q.sQ = sx; q.ldp = p.np; q.ldq = p.np; q.K = p.np;
+    q.C = A; q.Ct = A; q.sC = sa; q.sCt = sa; q.ldc = p.mp; q.ldct = p.mp;
+    q.tm = T; q.tn = T; q.sym = 1; q.tiles_per_mat = T * (T + 1) / 2;
+    q.alpha_pow = (t == 0) ? 2 : 0;
+    q.c_acc = 1.0f; q.c_e = 0.0f;
+    q.mvalid = p.mp; q.nvalid = p.mp;
+  } else if (stage == STAGE_POLY) {
+    q.P = A; q.Q = A; q.sP = sa; q.sQ = sa; q.ldp = p.mp; q.ldq = p.mp; q.K = p.mp;
+    q.C = B; q.Ct = B; q.sC = sa; q.sCt = sa; q.ldc = p.mp; q.ldct = p.mp;
+    q.Et = A; q.sEt = sa; q.lde = p.mp;
+    q.tm = T; q.tn = T; q.sym = 1; q.tiles_per_mat = T * (T + 1) / 2;
+    q.alpha_pow = 0;
+    q.c_acc = c; q.c_e = b; q.c_diag = a;
+    q.mvalid = p.mp; q.nvalid = p.mp;
+  } else {
+    const int TN = p.np / p.tile;
+    q.P = B; q.Q = Xt; q.sP = sa; q.sQ = sx; q.ldp = p.mp; q.ldq = p.mp; q.K = p.mp;
+    q.tm = T; q.tn = TN; q.sym = 0; q.tiles_per_mat = T * TN;
+    q.alpha_pow = (t == 0) ? 1 : 0;
+    q.c_acc = 1.0f; q.c_e = 0.0f;
+    const bool last = (t == steps - 1);
+    if (!last) {
+      q.C = Xn; q.sC = sx; q.ldc = p.np;
+      q.Ct = Xtn; q.sCt = sx; q.ldct = p.mp;
+      q.mvalid = p.mp; q.nvalid = p.np;
+    } else if (fin && fin->ptr) {
+      // write the result straight into the caller's dense output
+      q.mvalid = p.m; q.nvalid = p.n;
+      if (!p.tall) { q.C = fin->ptr; q.sC = fin->stride; q.ldc = fin->ld; }
+      else {
+        q.Ct = fin->ptr; q.sCt = fin->stride; q.ldct = fin->ld;
+        q.ct_vec = (fin->ld % 4 == 0) && aligned(fin->ptr, 8) && (fin->stride % 4 == 0);
+      }
+    } else {
+      q.mvalid = p.mp; q.nvalid = p.np;
+      if (!p.tall) { q.C = Xn; q.sC = sx; q.ldc = p.np; }
+      else { q.Ct = Xtn; q.sCt = sx; q.ldct = p.mp; }
+    }
+  }
+  return q;
+}
+
+int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c, void* ws,
+           const std::vector<FinalOut>* fins, hipStream_t s) {
+  static const int kinds[3] = {KIND_NS_SYRK, KIND_NS_POLY, KIND_NS_BX};
+  for (int t = 0; t < steps; ++t) {
+    for (int stage = 0; stage < 3; ++stage) {
+      for (int tile : {256, 128}) {
+        GemmLaunch L{};
+        int tiles = 0;
+        for (size_t g = 0; g < plans.size(); ++g) {
+          if (plans[g].tile != tile) continue;
+          GemmProb q = make_prob(plans[g], stage, t, steps, a, b, c, ws, fins ? &(*fins)[g] : nullptr);
+          L.prefix[L.nprob] = tiles;
+          L.p[L.nprob] = q;
+          tiles += plans[g].batch * q.tiles_per_mat;
+          ++L.nprob;
+        }
+        if (L.nprob == 0) continue;
+        L.prefix[L.nprob] = tiles;
+        MUON_LAUNCH(kinds[stage], s, launch_ns_gemm(L, tile, tiles, s));
+      }
+    }
+  }
+  return MUON_OK;
+}
+
+float update_scale(int mode, int rows, int cols, float rms) {
+  if (mode == MUON_SCALE_MOONLIGHT) return static_cast<float>(rms * sqrt(static_cast<double>(std::max(rows, cols))));
+  if (mode == MUON_SCALE_SPECTRAL) return static_cast<float>(sqrt(static_cast<double>(rows) / cols));
+  return 1.0f;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARG: return "invalid argument";
+    case MUON_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MUON_ERR_WORKSPACE: return "workspace missing or too small";
+    case MUON_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t muon_step_workspace_size(const muon_group_t* groups, int n_groups) {
+  if (check_groups(groups, n_groups) != MUON_OK) return 0;
+  size_t total = 0;
+  plans_for(groups, n_groups, total);
+  return total;
+}
+
+int muon_step_workspace_layout(const muon_group_t* groups, int n_groups, int g, int ns_steps,
+                               muon_ws_layout_t* out) {
+  int st = check_groups(groups, n_groups);
+  if (st != MUON_OK) return st;
+  if (!out || g < 0 || g >= n_groups || ns_steps < 1 || ns_steps > 64) return MUON_ERR_INVALID_ARG;
+  size_t total = 0;
+  std::vector<Plan> plans = plans_for(groups, n_groups, total);
+  const Plan& p = plans[g];
+  const int fin = ns_steps & 1;
+  out->o_offset = p.tall ? p.off_Xt[fin] : p.off_X[fin];
+  out->o_batch_stride = static_cast<int64_t>(p.mp) * p.np;
+  out->o_ld = p.tall ? p.mp : p.np;
+  out->inv_norm_offset = p.off_inv;
+  out->x0_offset = p.off_X[0];
+  out->x0_batch_stride = static_cast<int64_t>(p.mp) * p.np;
+  out->x0_ld = p.np;
+  return MUON_OK;
+}
+
+int muon_step(const muon_group_t* groups, int n_groups, int param_dtype, const muon_hparams_t* hp,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_groups(groups, n_groups);
+  if (st != MUON_OK) return st;
+  if (!hp || (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)) return MUON_ERR_INVALID_ARG;
+  if (hp->ns_steps < 1 || hp->ns_steps > 64) return MUON_ERR_INVALID_ARG;
+  if (hp->scale_mode < MUON_SCALE_MOONLIGHT || hp->scale_mode > MUON_SCALE_NONE) return MUON_ERR_INVALID_ARG;
+  if (!(hp->ns_eps >= 0.0f) || !isfinite(hp->lr) || !isfinite(hp->momentum) || !isfinite(hp->weight_decay))
+    return MUON_ERR_INVALID_ARG;
+  for (int g = 0; g < n_groups; ++g)
+    if (!groups[g].param || !groups[g].grad || !groups[g].momentum) return MUON_ERR_INVALID_ARG;
+  size_t need = 0;
+  std::vector<Plan> plans = plans_for(groups, n_groups, need);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
+
+  std::vector<PrepIn> ins;
+  for (int g = 0; g < n_groups; ++g) ins.push_back({groups[g].grad, groups[g].momentum});
+  st = launch_prep(plans, ins, param_dtype, hp->momentum, hp->nesterov ? 1 : 0, workspace, stream);
+  if (st != MUON_OK) return st;
+  st = launch_finalize(plans, hp->ns_eps, workspace, stream);
+  if (st != MUON_OK) return st;
+  st = run_ns(plans, hp->ns_steps, hp->ns_a, hp->ns_b, hp->ns_c, workspace, nullptr, stream);
+  if (st != MUON_OK) return st;
+
+  UpdateLaunch U{};
+  U.ngroups = n_groups;
+  int64_t blocks = 0;
+  const size_t esz = param_dtype == MUON_DTYPE_BF16 ? 2 : 4;
+  const int fin = hp->ns_steps & 1;
+  for (int g = 0; g < n_groups; ++g) {
+    const Plan& p = plans[g];
+    UpdateGroup& u = U.g[g];
+    u.W = groups[g].param;
+    u.O = at<bf16_t>(workspace, p.tall ? p.off_Xt[fin] : p.off_X[fin]);
+    u.bstride = p.bstride;
+    u.o_bstride = static_cast<int64_t>(p.mp) * p.np;
+    u.o_ld = p.tall ? p.mp : p.np;
+    u.rows = p.rows;
+    u.cols = p.cols;
+    u.batch = p.batch;
+    u.vec = (p.cols % 8 == 0) && (p.bstride % 8 == 0) && aligned(u.W, 8 * esz);
+    const int64_t per = (static_cast<int64_t>(p.rows) * p.cols + 2047) / 2048;
+    u.blocks = per * p.batch;
+    const float scale = update_scale(hp->scale_mode, p.rows, p.cols, hp->rms_target);
+    u.decay = static_cast<float>(1.0 - static_cast<double>(hp->lr) * hp->weight_decay);
+    u.step = static_cast<float>(static_cast<double>(hp->lr) * scale);
+    U.prefix[g] = blocks;
+    blocks += u.blocks;
+  }
+  U.prefix[n_groups] = blocks;
+  MUON_LAUNCH(KIND_PARAM_UPDATE, stream, launch_param_update(U, param_dtype, blocks, stream));
+  return MUON_OK;
+}
+
+size_t ns_workspace_size(int batch, int rows, int cols) {
+  if (!dims_ok(batch, rows, cols)) return 0;
+  size_t cursor = 0;
+  make_plan(batch, rows, cols, static_cast<int64_t>(rows) * cols, cursor);
+  return cursor;
+}
+
+int ns_orthogonalize(const void* in, int in_dtype, uint16_t* out, int batch, int rows, int cols,
+                     int64_t batch_stride, int steps, float a, float b, float c, float eps,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!in || !out || !dims_ok(batch, rows, cols)) return MUON_ERR_INVALID_ARG;
+  if (in_dtype != MUON_DTYPE_F32 && in_dtype != MUON_DTYPE_BF16) return MUON_ERR_INVALID_ARG;
+  if (batch_stride < static_cast<int64_t>(rows) * cols) return MUON_ERR_INVALID_ARG;
+  if (steps < 1 || steps > 64 || !(eps >= 0.0f)) return MUON_ERR_INVALID_ARG;
+  size_t need = 0;
+  std::vector<Plan> plans;
+  plans.push_back(make_plan(batch, rows, cols, batch_stride, need));
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
+  std::vector<PrepIn> ins{{in, nullptr}};
+  int st = launch_prep(plans, ins, in_dtype, 0.0f, 0, workspace, stream);
+  if (st != MUON_OK) return st;
+  st = launch_finalize(plans, eps, workspace, stream);
+  if (st != MUON_OK) return st;
+  std::vector<FinalOut> fins{{reinterpret_cast<bf16_t*>(out), static_cast<int64_t>(rows) * cols, cols}};
+  return run_ns(plans, steps, a, b, c, workspace, &fins, stream);
+}
+
+size_t qkclip_rowmax_workspace_size(int B, int T, int H) {
+  if (B < 1 || T < 1 || H < 1) return 0;
+  const int nqb = (T + 255) / 256;
+  return align_up(static_cast<size_t>(B) * H * nqb * sizeof(float));
+}
+
+int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int d_head, float logit_scale,
+                  int causal, float* s_max, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!Q || !K || !s_max || B < 1 || T < 1 || H < 1 || d_head < 1) return MUON_ERR_INVALID_ARG;
+  if (!(logit_scale > 0.0f) || !isfinite(logit_scale)) return MUON_ERR_INVALID_ARG;
+  if (d_head != 64 && d_head != 128 && d_head != 256) return MUON_ERR_UNSUPPORTED;
+  if (!aligned(Q, 16) || !aligned(K, 16)) return MUON_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * T * H * d_head > (int64_t(1) << 40)) return MUON_ERR_INVALID_ARG;
+  const int nqb = (T + 255) / 256;
+  if (static_cast<int64_t>(B) * H * nqb > (int64_t(1) << 31) - 1) return MUON_ERR_INVALID_ARG;
+  const size_t need = qkclip_rowmax_workspace_size(B, T, H);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return MUON_ERR_WORKSPACE;
+  float* partial = static_cast<float*>(workspace);
+  MUON_LAUNCH(KIND_QK_ROWMAX, stream,
+              launch_qk_rowmax(reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K), B, T, H,
+                               d_head, causal ? 1 : 0, partial, nqb, stream));
+  MUON_LAUNCH(KIND_QK_REDUCE, stream, launch_qk_reduce(partial, B, H, nqb, logit_scale, s_max, stream));
+  return MUON_OK;
+}
+
+int qkclip_rescale(void* Wq, void* Wk, int dtype, int H, int d_head, int d_model, const float* s_max, float tau,
+                   float alpha, int32_t* clipped, hipStream_t stream) {
+  if (!Wq || !Wk || !s_max || H < 1 || d_head < 1 || d_model < 1) return MUON_ERR_INVALID_ARG;
+  if (dtype != MUON_DTYPE_F32 && dtype != MUON_DTYPE_BF16) return MUON_ERR_INVALID_ARG;
+  if (!(tau > 0.0f) || !isfinite(tau) || !(alpha >= 0.0f && alpha <= 1.0f)) return MUON_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(d_head) * d_model > (int64_t(1) << 31) / 2) return MUON_ERR_INVALID_ARG;
+  MUON_LAUNCH(KIND_QK_RESCALE, stream,
+              launch_qk_rescale(Wq, Wk, dtype, H, d_head, d_model, s_max, tau, alpha, clipped, stream));
+  return MUON_OK;
+}
+
+int muon_profile_enable(int on) {
+  for (auto& r : g_prof) {
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  g_prof_on = on != 0;
+  return MUON_OK;
+}
+
+int muon_profile_collect(double* total_ms, int64_t* launches, int n_kinds) {
+  for (int k = 0; k < n_kinds; ++k) {
+    if (total_ms) total_ms[k] = 0.0;
+    if (launches) launches[k] = 0;
+  }
+  for (auto& r : g_prof) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return -MUON_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return -MUON_ERR_HIP;
+    if (r.kind < n_kinds) {
+      if (total_ms) total_ms[r.kind] += ms;
+      if (launches) launches[r.kind] += 1;
+    }
+  }
+  return KIND_COUNT;
+}
+
+const char* muon_kernel_kind_name(int kind) {
+  static const char* names[KIND_COUNT] = {"momentum_norm", "norm_finalize", "ns_syrk_xxt", "ns_syrk_poly",
+                                          "ns_gemm_bx",    "param_update",  "qk_rowmax",   "qk_reduce",
+                                          "qk_rescale"};
+  if (kind < 0 || kind >= KIND_COUNT) return "unknown";
+  return names[kind];
+}
+
+}  // extern "C"

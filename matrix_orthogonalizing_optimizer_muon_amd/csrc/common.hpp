@@ -1,0 +1,177 @@
+// Shared device helpers and launch descriptors for libmuon (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "../../include/muon.h"
+
+namespace muon {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest, ties to
+// even, and keeps NaN quiet.
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>{}) for i = 0..N-1.
+// Register arrays indexed only through such constants are promoted to
+// registers from the start (a runtime loop index, even one unrolled later,
+// can leave them in scratch or LDS).
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
+// This bijection hands each XCD one contiguous range of logical work items,
+// so the blocks an XCD runs at the same time share operands in its L2.
+__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+  const int per = nblocks / 8, rem = nblocks % 8;
+  const int x = b % 8, idx = b / 8;
+  return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
+}
+
+// Kernel kinds, used by the optional event profiler.
+enum KernelKind {
+  KIND_MOMENTUM_NORM = 0,
+  KIND_NORM_FINALIZE = 1,
+  KIND_NS_SYRK = 2,
+  KIND_NS_POLY = 3,
+  KIND_NS_BX = 4,
+  KIND_PARAM_UPDATE = 5,
+  KIND_QK_ROWMAX = 6,
+  KIND_QK_REDUCE = 7,
+  KIND_QK_RESCALE = 8,
+  KIND_COUNT = 9
+};
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz GEMM launch: C[i][j] = sum_k P[i][k] * Q[j][k] over
+// `batch` matrices of a problem, every problem of a launch sharing one tile
+// size.  Epilogue: v = s * (c_acc * acc + c_e * E(i, j) + c_diag [i == j]), where s is 1,
+// alpha[mat] or alpha[mat]^2, and E(i, j) is read as Et[j][i] (so that a
+// lane's four consecutive rows are one 8-byte load).
+// ---------------------------------------------------------------------------
+constexpr int kMaxProbs = MUON_MAX_GROUPS;
+
+struct GemmProb {
+  const bf16_t* P;
+  const bf16_t* Q;
+  const bf16_t* Et;
+  const float* alpha;
+  bf16_t* C;   // row-major output C[i][j], or null
+  bf16_t* Ct;  // transposed output Ct[j][i] (the mirror when sym), or null
+  int64_t sP, sQ, sEt, sC, sCt;  // per-matrix strides, elements
+  int ldp, ldq, lde, ldc, ldct;  // leading dimensions, elements
+  int K;                         // contraction length, multiple of 32
+  int tm, tn;                    // tiles along i and j
+  int tiles_per_mat;
+  int sym;          // 1: only tiles ti <= tj, written at (ti,tj) and mirrored
+  int alpha_pow;    // 0: s = 1, 1: s = alpha, 2: s = alpha^2
+  int mvalid, nvalid;  // outputs are written only for i < mvalid, j < nvalid
+  int ct_vec;       // 1 if Ct rows allow aligned 8-byte stores
+  float c_acc, c_e;
+  float c_diag;     // added on the diagonal i == j (before the scale s)
+};
+
+struct GemmLaunch {
+  int nprob;
+  int prefix[kMaxProbs + 1];
+  GemmProb p[kMaxProbs];
+};
+
+// ---------------------------------------------------------------------------
+// Elementwise launch descriptors.
+// ---------------------------------------------------------------------------
+struct MomentumGroup {
+  const void* G;      // grad (param dtype), or the input of ns_orthogonalize
+  float* M;           // momentum (null: no momentum, U = G)
+  int64_t bstride;    // elements between matrices of G / M
+  int rows, cols;     // original layout
+  int rp, cp;         // padded original layout (multiples of 64)
+  bf16_t* D1;         // U in its own layout, ld = cp, stride d_stride
+  bf16_t* D2;         // U transposed, ld = rp, stride d_stride
+  int64_t d_stride;   // rp * cp
+  double* partials;   // [batch][tiles_per_mat]
+  int tiles_r, tiles_c, tiles_per_mat;
+  int batch;
+  int vec;            // cols % 4 == 0 and bstride % 4 == 0
+};
+
+struct MomentumLaunch {
+  int ngroups;
+  int prefix[kMaxProbs + 1];  // block prefix over groups
+  MomentumGroup g[kMaxProbs];
+  float mu;
+  int nesterov;
+};
+
+struct FinalizeLaunch {
+  int ngroups;
+  int prefix[kMaxProbs + 1];  // matrix prefix over groups
+  const double* partials[kMaxProbs];
+  int tiles_per_mat[kMaxProbs];
+  float* inv_norm[kMaxProbs];
+  float eps;
+};
+
+struct UpdateGroup {
+  void* W;            // param, [batch][rows][cols], stride bstride
+  const bf16_t* O;    // orthogonalised direction in W's layout, ld = o_ld
+  int64_t bstride, o_bstride;
+  int o_ld;
+  int rows, cols, batch;
+  int vec;            // cols % 8 == 0, bstride % 8 == 0, o_ld % 8 == 0
+  int64_t blocks;     // blocks for this group
+  float decay;        // 1 - lr * wd
+  float step;         // lr * scale
+};
+
+struct UpdateLaunch {
+  int ngroups;
+  int64_t prefix[kMaxProbs + 1];
+  UpdateGroup g[kMaxProbs];
+};
+
+// Launchers (defined next to their kernels).  Each returns hipGetLastError().
+hipError_t launch_momentum_norm(const MomentumLaunch& L, int grad_dtype, int nblocks, hipStream_t s);
+hipError_t launch_norm_finalize(const FinalizeLaunch& L, int nmats, hipStream_t s);
+hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int nblocks, hipStream_t s);
+hipError_t launch_param_update(const UpdateLaunch& L, int param_dtype, int64_t nblocks, hipStream_t s);
+hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int H, int d_head,
+                            int causal, float* partial, int nqb, hipStream_t s);
+hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float logit_scale,
+                            float* s_max, hipStream_t s);
+hipError_t launch_qk_rescale(void* Wq, void* Wk, int dtype, int H, int d_head, int d_model,
+                             const float* s_max, float tau, float alpha, int32_t* clipped,
+                             hipStream_t s);
+
+// Profiler hooks (api.hip).
+void prof_begin(int kind, hipStream_t s);
+void prof_end(int kind, hipStream_t s);
+
+}  // namespace muon

@@ -1,0 +1,241 @@
+// HBM-bound passes of the Muon step: the momentum/Nesterov/Frobenius pass,
+// the per-matrix norm finalisation and the scaled, decayed parameter write.
+//
+// Momentum and lookahead follow "MuonClip", section 02 (M_t = mu M_{t-1} +
+// G_t, with the Nesterov lookahead U = G_t + mu M_t); the Frobenius
+// normalisation follows "Muon and MuonClip: orthogonalised updates for LLM
+// training", Newton-Schulz subsection (X_0 = G / ||G||_F); the parameter write
+// follows "MuonClip", section 03 (W_t = W_{t-1} - lr (scale O_t + wd W_{t-1})).
+#include "common.hpp"
+
+namespace muon {
+
+namespace {
+
+constexpr int kTile = 64;      // momentum tile edge (original layout)
+constexpr int kTrPitch = 66;   // LDS pitch of the transposed tile, bf16 units
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One block = one 64 x 64 tile of one matrix in its original layout,
+// covering the zero-padded extent so that every byte of the padded
+// Newton-Schulz inputs is written.  Writes M (in place), U rounded to bf16
+// in its own layout (D1) and transposed (D2), and the tile's sum of u^2.
+template <typename GT>
+__global__ __launch_bounds__(256) void momentum_norm_kernel(MomentumLaunch L) {
+  __shared__ __attribute__((aligned(16))) bf16_t tr[kTile * kTrPitch];
+  __shared__ double wsum[4];
+
+  int blk = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < L.ngroups && blk >= L.prefix[gi + 1]) ++gi;
+  const MomentumGroup& g = L.g[gi];
+  const int local = blk - L.prefix[gi];
+  const int mat = local / g.tiles_per_mat;
+  const int t = local - mat * g.tiles_per_mat;
+  const int tr_row = t / g.tiles_c, tr_col = t - tr_row * g.tiles_c;
+  const int i0 = tr_row * kTile, j0 = tr_col * kTile;
+
+  const GT* G = static_cast<const GT*>(g.G) + mat * g.bstride;
+  float* M = g.M ? g.M + mat * g.bstride : nullptr;
+  bf16_t* D1 = g.D1 + mat * g.d_stride;
+  bf16_t* D2 = g.D2 + mat * g.d_stride;
+
+  const int tid = threadIdx.x;
+  const int c0 = (tid & 15) * 4;
+  const int rsub = tid >> 4;
+  const float mu = L.mu;
+  double ss = 0.0;
+
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = rsub + 16 * p;
+    const int i = i0 + r;
+    float u[4];
+    if (i < g.rows && g.vec && j0 + c0 + 3 < g.cols) {
+      const int64_t e = static_cast<int64_t>(i) * g.cols + j0 + c0;
+      float gv[4];
+      if constexpr (sizeof(GT) == 2) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(G + e);
+        gv[0] = bf16_to_f32(raw.x & 0xffff);
+        gv[1] = bf16_to_f32(raw.x >> 16);
+        gv[2] = bf16_to_f32(raw.y & 0xffff);
+        gv[3] = bf16_to_f32(raw.y >> 16);
+      } else {
+        const float4 raw = *reinterpret_cast<const float4*>(G + e);
+        gv[0] = raw.x; gv[1] = raw.y; gv[2] = raw.z; gv[3] = raw.w;
+      }
+      if (M) {
+        float4 mv = *reinterpret_cast<const float4*>(M + e);
+        float m[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          m[q] = fmaf(mu, m[q], gv[q]);
+          u[q] = L.nesterov ? fmaf(mu, m[q], gv[q]) : m[q];
+        }
+        *reinterpret_cast<float4*>(M + e) = make_float4(m[0], m[1], m[2], m[3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) u[q] = gv[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + c0 + q;
+        u[q] = 0.0f;
+        if (i < g.rows && j < g.cols) {
+          const int64_t e = static_cast<int64_t>(i) * g.cols + j;
+          float gv;
+          if constexpr (sizeof(GT) == 2) gv = bf16_to_f32(reinterpret_cast<const bf16_t*>(G)[e]);
+          else gv = static_cast<float>(G[e]);
+          if (M) {
+            const float m = fmaf(mu, M[e], gv);
+            M[e] = m;
+            u[q] = L.nesterov ? fmaf(mu, m, gv) : m;
+          } else {
+            u[q] = gv;
+          }
+        }
+      }
+    }
+    bf16_t ub[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ss += static_cast<double>(u[q]) * static_cast<double>(u[q]);
+      ub[q] = f32_to_bf16(u[q]);
+      tr[(c0 + q) * kTrPitch + r] = ub[q];
+    }
+    // U in its own layout (padded extent always written).
+    uint2 packed;
+    packed.x = static_cast<uint32_t>(ub[0]) | (static_cast<uint32_t>(ub[1]) << 16);
+    packed.y = static_cast<uint32_t>(ub[2]) | (static_cast<uint32_t>(ub[3]) << 16);
+    *reinterpret_cast<uint2*>(D1 + static_cast<int64_t>(i) * g.cp + j0 + c0) = packed;
+  }
+
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+
+  // Transposed tile: row jj of D2 (original column j0 + jj), 16 consecutive
+  // original rows per thread.
+  {
+    const int jj = tid >> 2;
+    const int ii = (tid & 3) * 16;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tr + jj * kTrPitch + ii);
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = src[q];
+    bf16_t* dst = D2 + static_cast<int64_t>(j0 + jj) * g.rp + i0 + ii;
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  if (tid == 0) {
+    g.partials[static_cast<int64_t>(mat) * g.tiles_per_mat + t] =
+        ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  }
+}
+
+// One block per matrix: fixed-order sum of the tile partials, then
+// 1 / (sqrt(sum) + eps).
+__global__ __launch_bounds__(64) void norm_finalize_kernel(FinalizeLaunch L) {
+  const int blk = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < L.ngroups && blk >= L.prefix[gi + 1]) ++gi;
+  const int mat = blk - L.prefix[gi];
+  const int n = L.tiles_per_mat[gi];
+  const double* p = L.partials[gi] + static_cast<int64_t>(mat) * n;
+  double s = 0.0;
+  for (int k = threadIdx.x; k < n; k += 64) s += p[k];
+  s = wave_sum(s);
+  if (threadIdx.x == 0) {
+    L.inv_norm[gi][mat] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(L.eps)));
+  }
+}
+
+// W <- decay * W - step * O over one group; 8 elements per thread.
+template <typename WT>
+__global__ __launch_bounds__(256) void param_update_kernel(UpdateLaunch L) {
+  const int64_t blk = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < L.ngroups && blk >= L.prefix[gi + 1]) ++gi;
+  const UpdateGroup& g = L.g[gi];
+  const int64_t local = blk - L.prefix[gi];
+  const int64_t per_mat = g.blocks / g.batch;
+  const int mat = static_cast<int>(local / per_mat);
+  const int64_t e0 = (local - mat * per_mat) * 2048 + threadIdx.x * 8;
+  const int64_t n = static_cast<int64_t>(g.rows) * g.cols;
+  if (e0 >= n) return;
+  WT* W = static_cast<WT*>(g.W) + mat * g.bstride;
+  const bf16_t* O = g.O + mat * g.o_bstride;
+  const float decay = g.decay, step = g.step;
+  if (g.vec && e0 + 7 < n) {
+    const int i = static_cast<int>(e0 / g.cols), j = static_cast<int>(e0 - static_cast<int64_t>(i) * g.cols);
+    const uint4 ov = *reinterpret_cast<const uint4*>(O + static_cast<int64_t>(i) * g.o_ld + j);
+    float o[8];
+    o[0] = bf16_to_f32(ov.x & 0xffff); o[1] = bf16_to_f32(ov.x >> 16);
+    o[2] = bf16_to_f32(ov.y & 0xffff); o[3] = bf16_to_f32(ov.y >> 16);
+    o[4] = bf16_to_f32(ov.z & 0xffff); o[5] = bf16_to_f32(ov.z >> 16);
+    o[6] = bf16_to_f32(ov.w & 0xffff); o[7] = bf16_to_f32(ov.w >> 16);
+    if constexpr (sizeof(WT) == 2) {
+      uint4 wv = *reinterpret_cast<const uint4*>(W + e0);
+      uint32_t* wp = reinterpret_cast<uint32_t*>(&wv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = fmaf(-step, o[2 * q], decay * bf16_to_f32(wp[q] & 0xffff));
+        const float hi = fmaf(-step, o[2 * q + 1], decay * bf16_to_f32(wp[q] >> 16));
+        wp[q] = pack2_bf16(lo, hi);
+      }
+      *reinterpret_cast<uint4*>(W + e0) = wv;
+    } else {
+      float4* wp = reinterpret_cast<float4*>(W + e0);
+      float4 a = wp[0], b = wp[1];
+      a.x = fmaf(-step, o[0], decay * a.x); a.y = fmaf(-step, o[1], decay * a.y);
+      a.z = fmaf(-step, o[2], decay * a.z); a.w = fmaf(-step, o[3], decay * a.w);
+      b.x = fmaf(-step, o[4], decay * b.x); b.y = fmaf(-step, o[5], decay * b.y);
+      b.z = fmaf(-step, o[6], decay * b.z); b.w = fmaf(-step, o[7], decay * b.w);
+      wp[0] = a; wp[1] = b;
+    }
+  } else {
+    for (int q = 0; q < 8; ++q) {
+      const int64_t e = e0 + q;
+      if (e >= n) break;
+      const int i = static_cast<int>(e / g.cols), j = static_cast<int>(e - static_cast<int64_t>(i) * g.cols);
+      const float o = bf16_to_f32(O[static_cast<int64_t>(i) * g.o_ld + j]);
+      if constexpr (sizeof(WT) == 2) {
+        bf16_t* w = reinterpret_cast<bf16_t*>(W) + e;
+        *w = f32_to_bf16(fmaf(-step, o, decay * bf16_to_f32(*w)));
+      } else {
+        W[e] = fmaf(-step, o, decay * W[e]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_momentum_norm(const MomentumLaunch& L, int grad_dtype, int nblocks, hipStream_t s) {
+  if (grad_dtype == MUON_DTYPE_BF16)
+    hipLaunchKernelGGL(momentum_norm_kernel<bf16_t>, dim3(nblocks), dim3(256), 0, s, L);
+  else
+    hipLaunchKernelGGL(momentum_norm_kernel<float>, dim3(nblocks), dim3(256), 0, s, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const FinalizeLaunch& L, int nmats, hipStream_t s) {
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(nmats), dim3(64), 0, s, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_param_update(const UpdateLaunch& L, int param_dtype, int64_t nblocks, hipStream_t s) {
+  if (param_dtype == MUON_DTYPE_BF16)
+    hipLaunchKernelGGL(param_update_kernel<bf16_t>, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, s, L);
+  else
+    hipLaunchKernelGGL(param_update_kernel<float>, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, s, L);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,247 @@
+// Newton-Schulz matrix products on CDNA4 bf16 MFMA ("Muon and MuonClip:
+// orthogonalised updates for LLM training", section 2, Newton-Schulz
+// subsection: A = X X^T, B = b A + c A A, X <- a X + B X; "MuonClip",
+// section 02, quintic step on the cheaper orientation).
+//
+// Every product of the iteration is an "NT" contraction whose two operands
+// are row-major with the contraction index contiguous:
+//   A = X X^T                P = Q = X  (m x n),  K = n, symmetric output
+//   B = a I + b A + c A A^T  P = Q = A  (m x m),  K = m, symmetric output (A = A^T)
+//   X' = B X                 P = B,  Q = X^T (n x m), K = m
+// (a X + (b A + c A A) X is computed as (a I + b A + c A A) X: one rounding of
+// the polynomial matrix, no a X term in the last product.)
+// so both MFMA operands are 16-byte row segments, staged through LDS.  The
+// symmetric products compute only tiles ti <= tj and write each off-diagonal
+// tile twice (in place and mirrored).  X is kept in both layouts (X and X^T):
+// the epilogue of X' writes both, so no transpose pass is ever needed.
+//
+// Tiling: TILE x TILE output per 256-thread block, 2 x 2 waves, each wave a
+// (TILE/2) x (TILE/2) sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16),
+// K staged 32 at a time in double-buffered, padded LDS.
+#include <utility>
+
+#include "common.hpp"
+
+namespace muon {
+
+namespace {
+
+constexpr int kBK = 64;
+constexpr int kPitch = kBK + 8;  // padded LDS row (bf16): 144 bytes, conflict-free b128 reads
+
+struct EpiArgs {
+  float ca, ce, cd;
+  bf16_t* C;
+  bf16_t* Ct;
+  const bf16_t* Et;
+  int ldc, ldct, lde, mvalid, nvalid, ct_vec;
+  int i0, j0;  // this lane's first row and its column inside block (0, 0)
+};
+
+// Epilogue of one 32x32 MFMA block (a, b): four groups of four consecutive
+// rows per lane.  Compile-time block indices keep the accumulators in
+// registers.
+template <int A, int B>
+__device__ __forceinline__ void epilogue_block(const f32x16_t& acc, const EpiArgs& e) {
+  const int j = e.j0 + 32 * B;
+  if (j >= e.nvalid) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = e.i0 + 32 * A + 8 * q;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = e.ca * acc[4 * q + r] + ((i + r == j) ? e.cd : 0.0f);
+    if (e.Et) {
+      const uint2 ev = *reinterpret_cast<const uint2*>(e.Et + static_cast<int64_t>(j) * e.lde + i);
+      v[0] = fmaf(e.ce, bf16_to_f32(ev.x & 0xffff), v[0]);
+      v[1] = fmaf(e.ce, bf16_to_f32(ev.x >> 16), v[1]);
+      v[2] = fmaf(e.ce, bf16_to_f32(ev.y & 0xffff), v[2]);
+      v[3] = fmaf(e.ce, bf16_to_f32(ev.y >> 16), v[3]);
+    }
+    bf16_t o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16(v[r]);
+    if (e.C) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (i + r < e.mvalid) e.C[static_cast<int64_t>(i + r) * e.ldc + j] = o[r];
+    }
+    if (e.Ct) {
+      bf16_t* dst = e.Ct + static_cast<int64_t>(j) * e.ldct + i;
+      if (e.ct_vec && i + 3 < e.mvalid) {
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16);
+        pk.y = static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16);
+        *reinterpret_cast<uint2*>(dst) = pk;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (i + r < e.mvalid) dst[r] = o[r];
+      }
+    }
+  }
+}
+
+template <int F, int... Is>
+__device__ __forceinline__ void epilogue_all(const f32x16_t (&acc)[F][F], const EpiArgs& e,
+                                             std::integer_sequence<int, Is...>) {
+  (epilogue_block<Is / F, Is % F>(acc[Is / F][Is % F], e), ...);
+}
+
+template <int TILE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ns_gemm_kernel(GemmLaunch L) {
+  constexpr int WT = TILE / 2;       // wave sub-tile edge
+  constexpr int F = WT / 32;         // 32x32 MFMA blocks per wave edge
+  constexpr int CPR = kBK / 8;        // 16-byte chunks per tile row of a K slice
+  constexpr int RPP = 256 / CPR;      // tile rows covered by one pass of 256 threads
+  constexpr int NCH = TILE / RPP;     // passes (chunks per thread per operand)
+  static_assert(TILE % RPP == 0, "staging map must cover the tile exactly");
+
+  __shared__ __attribute__((aligned(16))) bf16_t sP[2][TILE * kPitch];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][TILE * kPitch];
+
+  // ---- block -> (problem, matrix, tile)
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  int gi = 0;
+  while (gi + 1 < L.nprob && lin >= L.prefix[gi + 1]) ++gi;
+  const GemmProb& p = L.p[gi];
+  const int local = lin - L.prefix[gi];
+  const int mat = local / p.tiles_per_mat;
+  int t = local - mat * p.tiles_per_mat;
+  int ti, tj;
+  if (p.sym) {
+    ti = 0;
+    int rowlen = p.tm;
+    while (t >= rowlen) { t -= rowlen; ++ti; --rowlen; }
+    tj = ti + t;
+  } else {
+    // groups of 8 tile-rows, column-major inside a group
+    constexpr int GM = 8;
+    const int gsz = GM * p.tn;
+    const int grp = t / gsz;
+    const int first = grp * GM;
+    const int gm = min(p.tm - first, GM);
+    const int r = t - grp * gsz;
+    ti = first + r % gm;
+    tj = r / gm;
+  }
+
+  const bf16_t* Pg = p.P + mat * p.sP + static_cast<int64_t>(ti) * TILE * p.ldp;
+  const bf16_t* Qg = p.Q + mat * p.sQ + static_cast<int64_t>(tj) * TILE * p.ldq;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr0 = (wave >> 1) * WT;  // wave row offset in the tile
+  const int wc0 = (wave & 1) * WT;   // wave col offset in the tile
+
+  // global -> register staging map: chunk c of this thread covers tile row
+  // (tid / CPR + RPP * c), 8 bf16 at column 8 * (tid % CPR) of the K slice.
+  const int lrow = tid / CPR;
+  const int lkc = (tid % CPR) * 8;
+
+  const bf16_t* gP[NCH];
+  const bf16_t* gQ[NCH];
+  int sOff[NCH];
+  static_for<NCH>([&](auto c) {
+    const int row = lrow + RPP * c;
+    gP[c] = Pg + static_cast<int64_t>(row) * p.ldp + lkc;
+    gQ[c] = Qg + static_cast<int64_t>(row) * p.ldq + lkc;
+    sOff[c] = row * kPitch + lkc;
+  });
+  u32x4_t rP[NCH], rQ[NCH];
+
+  f32x16_t acc[F][F];
+  static_for<F * F>([&](auto ab) { acc[ab / F][ab % F] = f32x16_t{}; });
+
+  const int KT = p.K / kBK;
+  static_for<NCH>([&](auto c) {
+    rP[c] = *reinterpret_cast<const u32x4_t*>(gP[c]);
+    rQ[c] = *reinterpret_cast<const u32x4_t*>(gQ[c]);
+  });
+  static_for<NCH>([&](auto c) {
+    *reinterpret_cast<u32x4_t*>(&sP[0][sOff[c]]) = rP[c];
+    *reinterpret_cast<u32x4_t*>(&sQ[0][sOff[c]]) = rQ[c];
+  });
+  __syncthreads();
+
+  const int frow = lane & 31;        // fragment row inside a 32-block
+  const int fk = (lane >> 5) * 8;    // fragment K offset (0 or 8)
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const int k1 = (kt + 1) * kBK;
+      static_for<NCH>([&](auto c) {
+        rP[c] = *reinterpret_cast<const u32x4_t*>(gP[c] + k1);
+        rQ[c] = *reinterpret_cast<const u32x4_t*>(gQ[c] + k1);
+      });
+    }
+    const bf16_t* sPc = sP[cur];
+    const bf16_t* sQc = sQ[cur];
+    // Fragments of K-substep s+1 are read from LDS before the MFMAs of
+    // substep s are issued, so LDS latency hides behind matrix work.
+    bf16x8_t fa[2][F], fb[2][F];
+    auto read_frags = [&](auto s, auto slot) {
+      static_for<F>([&](auto a) {
+        fa[slot][a] = *reinterpret_cast<const bf16x8_t*>(&sPc[(wr0 + a * 32 + frow) * kPitch + s * 16 + fk]);
+      });
+      static_for<F>([&](auto b) {
+        fb[slot][b] = *reinterpret_cast<const bf16x8_t*>(&sQc[(wc0 + b * 32 + frow) * kPitch + s * 16 + fk]);
+      });
+    };
+    read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    static_for<kBK / 16>([&](auto s) {
+      constexpr int S = decltype(s)::value;
+      constexpr int slot = S & 1;
+      if constexpr (S + 1 < kBK / 16)
+        read_frags(std::integral_constant<int, S + 1>{}, std::integral_constant<int, slot ^ 1>{});
+      static_for<F * F>([&](auto ab) {
+        constexpr int A = decltype(ab)::value / F, B = decltype(ab)::value % F;
+        acc[A][B] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][A], fb[slot][B], acc[A][B], 0, 0, 0);
+      });
+    });
+    if (more) {
+      static_for<NCH>([&](auto c) {
+        *reinterpret_cast<u32x4_t*>(&sP[cur ^ 1][sOff[c]]) = rP[c];
+        *reinterpret_cast<u32x4_t*>(&sQ[cur ^ 1][sOff[c]]) = rQ[c];
+      });
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Element e of acc[a][b] holds C[i][j] with
+  //   i = tile_i0 + wr0 + 32 a + 8 (e / 4) + 4 (lane / 32) + (e % 4),
+  //   j = tile_j0 + wc0 + 32 b + (lane % 32).
+  float sc = 1.0f;
+  if (p.alpha_pow) {
+    const float al = p.alpha[mat];
+    sc = (p.alpha_pow == 2) ? al * al : al;
+  }
+  EpiArgs e;
+  e.ca = p.c_acc * sc;
+  e.ce = p.c_e * sc;
+  e.cd = p.c_diag * sc;
+  e.C = p.C ? p.C + mat * p.sC : nullptr;
+  e.Ct = (p.Ct && (!p.sym || ti != tj)) ? p.Ct + mat * p.sCt : nullptr;
+  e.Et = p.Et ? p.Et + mat * p.sEt : nullptr;
+  e.ldc = p.ldc; e.ldct = p.ldct; e.lde = p.lde;
+  e.mvalid = p.mvalid; e.nvalid = p.nvalid; e.ct_vec = p.ct_vec;
+  e.i0 = ti * TILE + wr0 + 4 * (lane >> 5);
+  e.j0 = tj * TILE + wc0 + (lane & 31);
+  epilogue_all<F>(acc, e, std::make_integer_sequence<int, F * F>{});
+}
+
+}  // namespace
+
+hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int nblocks, hipStream_t s) {
+  if (tile == 256)
+    hipLaunchKernelGGL(ns_gemm_kernel<256>, dim3(nblocks), dim3(256), 0, s, L);
+  else
+    hipLaunchKernelGGL(ns_gemm_kernel<128>, dim3(nblocks), dim3(256), 0, s, L);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,273 @@
+// QK-Clip on CDNA4: the per-head maximum pre-softmax logit and the per-head
+// W_q / W_k rescale.
+//
+// S_max^h = logit_scale * max over batch rows, i and j (j <= i when causal)
+// of q_i^h . k_j^h ("Muon and MuonClip: orthogonalised updates for LLM
+// training", "The exploding-logit problem"; "MuonClip", section 05 per-head
+// signal).  gamma_h = min(1, tau / S_max^h); rows of head h in W_q scale by
+// gamma^alpha and in W_k by gamma^(1 - alpha) ("MuonClip", section 05
+// balanced rescale; "About Muon: Muon At Scale", "When Softmax Collapses").
+//
+// The statistic is a causal Q K^T contraction reduced by max, so it runs as
+// a flash-style MFMA loop: one block per (batch row, head, 256 queries), the
+// queries' fragments held in registers, 64-key blocks staged through LDS,
+// the logits never stored.  Maxima are reduced across the wavefront with
+// cross-lane max, across the block through LDS, and across blocks by a
+// second, fixed-order kernel (no atomics, no initialisation pass).
+#include "common.hpp"
+
+namespace muon {
+
+namespace {
+
+constexpr int kQB = 256;   // queries per block (4 waves x 64)
+constexpr int kKB = 64;    // keys per LDS stage
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void qk_rowmax_kernel(const bf16_t* __restrict__ Q,
+                                                        const bf16_t* __restrict__ K, int B,
+                                                        int T, int H, int causal,
+                                                        float* __restrict__ partial, int nqb) {
+  constexpr int PITCH = D + 8;           // padded LDS row, bf16 units
+  constexpr int KS = D / 16;             // MFMA K-substeps
+  constexpr int NCH = kKB * (D / 8) / 256;  // 16-byte chunks per thread per key block
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][kKB * PITCH];
+  __shared__ float wmax[4];
+  __shared__ int wnan[4];
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nqb;
+  const int qb = nqb - 1 - (lin - bh * nqb);  // heaviest query blocks first
+  const int b = bh / H, h = bh - b * H;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row_stride = static_cast<int64_t>(H) * D;
+  const bf16_t* Qb = Q + static_cast<int64_t>(b) * T * row_stride + static_cast<int64_t>(h) * D;
+  const bf16_t* Kb = K + static_cast<int64_t>(b) * T * row_stride + static_cast<int64_t>(h) * D;
+
+  const int r0 = qb * kQB + wave * 64;  // first query row of this wave
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+
+  // Query fragments for the wave's 64 rows: [row block 0/1][K-substep].
+  bf16x8_t qf[2][KS];
+  static_for<2>([&](auto a) {
+    const int row = r0 + a * 32 + frow;
+    static_for<KS>([&](auto s) {
+      if (row < T) {
+        qf[a][s] = *reinterpret_cast<const bf16x8_t*>(Qb + row * row_stride + s * 16 + fk);
+      } else {
+        qf[a][s] = bf16x8_t{};
+      }
+    });
+  });
+
+  const int kend = causal ? min(T, (qb + 1) * kQB) : T;
+  const int nkb = (kend + kKB - 1) / kKB;
+
+  // key staging map: chunk c covers key (tid / (D/8) + c * 256/(D/8)), column 8*(tid % (D/8))
+  constexpr int CPR = D / 8;  // chunks per key row
+  u32x4_t rk[NCH];
+  auto gload = [&](int kb) {
+    static_for<NCH>([&](auto c) {
+      const int kr = tid / CPR + c * (256 / CPR);
+      const int j = kb * kKB + kr;
+      if (j < T)
+        rk[c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + (tid % CPR) * 8);
+      else
+        rk[c] = u32x4_t{};
+    });
+  };
+  auto sstore = [&](int buf) {
+    static_for<NCH>([&](auto c) {
+      const int kr = tid / CPR + c * (256 / CPR);
+      *reinterpret_cast<u32x4_t*>(&sK[buf][kr * PITCH + (tid % CPR) * 8]) = rk[c];
+    });
+  };
+
+  float m = -INFINITY;
+  int has_nan = 0;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const bool more = kb + 1 < nkb;
+    if (more) gload(kb + 1);
+    const int c0 = kb * kKB;
+    // This wave's rows r0 .. r0+63 see keys c0 .. c0+63 unless all are masked.
+    const bool any = (r0 < T) && (!causal || c0 <= r0 + 63);
+    if (any) {
+      f32x16_t acc[2][2];
+      static_for<4>([&](auto ab) { acc[ab / 2][ab % 2] = f32x16_t{}; });
+      const bf16_t* sKc = sK[cur];
+      static_for<KS>([&](auto s) {
+        bf16x8_t kf[2];
+        static_for<2>([&](auto n) {
+          kf[n] = *reinterpret_cast<const bf16x8_t*>(&sKc[(n * 32 + frow) * PITCH + s * 16 + fk]);
+        });
+        static_for<4>([&](auto ab) {
+          constexpr int A = decltype(ab)::value / 2, N = decltype(ab)::value % 2;
+          acc[A][N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[A][s], kf[N], acc[A][N], 0, 0, 0);
+        });
+      });
+      // Unmasked block: every (i, j) valid.
+      const bool full = (!causal || c0 + 63 <= r0) && (r0 + 63 < T) && (c0 + 63 < T);
+      static_for<4>([&](auto ab) {
+        constexpr int A = decltype(ab)::value / 2, N = decltype(ab)::value % 2;
+        const int j = c0 + N * 32 + (lane & 31);
+        static_for<16>([&](auto e) {
+          constexpr int E = decltype(e)::value;
+          const float v = acc[A][N][E];
+          const int i = r0 + A * 32 + 8 * (E / 4) + 4 * (lane >> 5) + (E % 4);
+          const bool ok = full || (i < T && j < T && (!causal || j <= i));
+          if (ok) {
+            m = fmaxf(m, v);
+            has_nan |= (v != v);
+          }
+        });
+      });
+    }
+    if (more) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  m = wave_max(m);
+  has_nan = __any(has_nan) ? 1 : 0;
+  if (lane == 0) {
+    wmax[wave] = m;
+    wnan[wave] = has_nan;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float r = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (wnan[0] | wnan[1] | wnan[2] | wnan[3]) r = __uint_as_float(0x7fc00000u);
+    partial[(static_cast<int64_t>(b) * H + h) * nqb + qb] = r;
+  }
+}
+
+// s_max[h] = logit_scale * max over (b, query block) of the partial maxima,
+// NaN if any partial is NaN.
+__global__ __launch_bounds__(64) void qk_reduce_kernel(const float* __restrict__ partial, int B,
+                                                       int H, int nqb, float logit_scale,
+                                                       float* __restrict__ s_max) {
+  const int h = blockIdx.x;
+  float m = -INFINITY;
+  int nan = 0;
+  const int n = B * nqb;
+  for (int k = threadIdx.x; k < n; k += 64) {
+    const int b = k / nqb, q = k - b * nqb;
+    const float v = partial[(static_cast<int64_t>(b) * H + h) * nqb + q];
+    nan |= (v != v);
+    m = fmaxf(m, v);
+  }
+  m = wave_max(m);
+  nan = __any(nan);
+  if (threadIdx.x == 0) s_max[h] = nan ? __uint_as_float(0x7fc00000u) : m * logit_scale;
+}
+
+// Rescale the rows of one head in W_q (z = 0) or W_k (z = 1).
+template <typename WT>
+__global__ __launch_bounds__(256) void qk_rescale_kernel(WT* __restrict__ Wq, WT* __restrict__ Wk,
+                                                         int d_head, int d_model,
+                                                         const float* __restrict__ s_max, float tau,
+                                                         float alpha, int32_t* __restrict__ clipped,
+                                                         int vec) {
+  const int h = blockIdx.y, z = blockIdx.z;
+  const float s = s_max[h];
+  const bool finite = (__float_as_uint(s) & 0x7f800000u) != 0x7f800000u;
+  const bool clip = finite && (s > tau);
+  if (clipped && blockIdx.x == 0 && z == 0 && threadIdx.x == 0) clipped[h] = finite ? (clip ? 1 : 0) : -1;
+  if (!clip) return;
+  const float gamma = tau / s;
+  const float ex = (z == 0) ? alpha : 1.0f - alpha;
+  float f;
+  if (ex == 0.5f) f = sqrtf(gamma);
+  else if (ex == 1.0f) f = gamma;
+  else if (ex == 0.0f) f = 1.0f;
+  else f = powf(gamma, ex);
+  WT* W = (z == 0 ? Wq : Wk) + static_cast<int64_t>(h) * d_head * d_model;
+  const int64_t n = static_cast<int64_t>(d_head) * d_model;
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (e0 >= n) return;
+  if (vec && e0 + 7 < n) {
+    if constexpr (sizeof(WT) == 2) {
+      u32x4_t w = *reinterpret_cast<const u32x4_t*>(W + e0);
+      static_for<4>([&](auto q) {
+        constexpr int Qi = decltype(q)::value;
+        const float lo = bf16_to_f32(w[Qi] & 0xffff) * f;
+        const float hi = bf16_to_f32(w[Qi] >> 16) * f;
+        w[Qi] = pack2_bf16(lo, hi);
+      });
+      *reinterpret_cast<u32x4_t*>(W + e0) = w;
+    } else {
+      f32x4_t* p = reinterpret_cast<f32x4_t*>(W + e0);
+      p[0] = p[0] * f;
+      p[1] = p[1] * f;
+    }
+  } else {
+    for (int q = 0; q < 8 && e0 + q < n; ++q) {
+      if constexpr (sizeof(WT) == 2) {
+        bf16_t* w = reinterpret_cast<bf16_t*>(W) + e0 + q;
+        *w = f32_to_bf16(bf16_to_f32(*w) * f);
+      } else {
+        W[e0 + q] *= f;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int H, int d_head,
+                            int causal, float* partial, int nqb, hipStream_t s) {
+  const int nblocks = B * H * nqb;
+  switch (d_head) {
+    case 64:
+      hipLaunchKernelGGL(qk_rowmax_kernel<64>, dim3(nblocks), dim3(256), 0, s, Q, K, B, T, H, causal, partial, nqb);
+      break;
+    case 128:
+      hipLaunchKernelGGL(qk_rowmax_kernel<128>, dim3(nblocks), dim3(256), 0, s, Q, K, B, T, H, causal, partial, nqb);
+      break;
+    case 256:
+      hipLaunchKernelGGL(qk_rowmax_kernel<256>, dim3(nblocks), dim3(256), 0, s, Q, K, B, T, H, causal, partial, nqb);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float logit_scale,
+                            float* s_max, hipStream_t s) {
+  hipLaunchKernelGGL(qk_reduce_kernel, dim3(H), dim3(64), 0, s, partial, B, H, nqb, logit_scale, s_max);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_rescale(void* Wq, void* Wk, int dtype, int H, int d_head, int d_model,
+                             const float* s_max, float tau, float alpha, int32_t* clipped,
+                             hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(d_head) * d_model;
+  const int bx = static_cast<int>((n + 2047) / 2048);
+  const int vec = (d_model % 8 == 0) &&
+                  (reinterpret_cast<uintptr_t>(Wq) % 16 == 0) && (reinterpret_cast<uintptr_t>(Wk) % 16 == 0) &&
+                  (dtype == MUON_DTYPE_BF16 ? true : (d_model % 8 == 0));
+  const int vec_ok = dtype == MUON_DTYPE_BF16 ? vec : (vec && (reinterpret_cast<uintptr_t>(Wq) % 32 == 0));
+  if (dtype == MUON_DTYPE_BF16)
+    hipLaunchKernelGGL(qk_rescale_kernel<bf16_t>, dim3(bx, H, 2), dim3(256), 0, s,
+                       static_cast<bf16_t*>(Wq), static_cast<bf16_t*>(Wk), d_head, d_model, s_max, tau,
+                       alpha, clipped, vec_ok);
+  else
+    hipLaunchKernelGGL(qk_rescale_kernel<float>, dim3(bx, H, 2), dim3(256), 0, s,
+                       static_cast<float*>(Wq), static_cast<float*>(Wk), d_head, d_model, s_max, tau,
+                       alpha, clipped, vec_ok);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -245,3 +245,39 @@ def random_qk(seed: int, batch: int, seq: int, heads: int, d_head: int, std: flo
     Q = f32_to_bf16_bits(gaussian(g, (batch, seq, heads, d_head), std))
     K = f32_to_bf16_bits(gaussian(g, (batch, seq, heads, d_head), std))
     return Q, K
+
+
+# ----------------------------------------------------------------------------
+# bulk fills on the GPU (large workloads); torch's seeded generator
+# ----------------------------------------------------------------------------
+
+def bulk_normal_torch(shape, std, seed, device, dtype):
+    """N(0, std^2) of `shape` drawn on `device` from a torch generator seeded
+    with `seed`, cast (nearest-even) to `dtype`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(dtype)
+
+
+def qk_inputs_torch(seed, batch, seq, heads, d_head, d_model, designated, targets, device,
+                    causal=True):
+    """The same recipe as qk_inputs, drawn on the GPU: X_act, W_q, W_k (bf16)
+    with `designated` seeded heads scaled towards `targets`.  Returns
+    dict(X, Wq, Wk, designated_heads)."""
+    import torch
+    X = bulk_normal_torch((batch * seq, d_model), 1.0, seed, device, torch.bfloat16)
+    std = 1.0 / math.sqrt(d_model)
+    Wq = bulk_normal_torch((heads * d_head, d_model), std, seed + 1, device, torch.float32)
+    Wk = bulk_normal_torch((heads * d_head, d_model), std, seed + 2, device, torch.float32)
+    heads_sel = np.sort(rng(seed).choice(heads, size=designated, replace=False))
+    pairs = batch * (seq * (seq + 1) / 2 if causal else seq * seq)
+    m0 = expected_gaussian_max(pairs)
+    for h, t in zip(heads_sel, list(targets)[:designated]):
+        s = math.sqrt(float(t) / m0)
+        Wq[h * d_head:(h + 1) * d_head] *= s
+        Wk[h * d_head:(h + 1) * d_head] *= s
+    return dict(X=X, Wq=Wq.to(torch.bfloat16), Wk=Wk.to(torch.bfloat16), designated_heads=heads_sel)

@@ -1,0 +1,91 @@
+"""CPU checks of the boundary: the C-ABI library loads and exports every
+function include/muon.h declares; host-side argument validation returns its
+documented status codes without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import matrix_orthogonalizing_optimizer_muon_amd as mm
+    if not os.path.exists(mm.library_path()):
+        pytest.skip("libmuon.so not built")
+    return mm.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ["muon_step", "ns_orthogonalize", "qkclip_rowmax", "qkclip_rescale"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.muon_status_string(s)
+
+
+def test_host_validation_without_gpu(lib):
+    import matrix_orthogonalizing_optimizer_muon_amd as mm
+    # null groups
+    assert lib.muon_step(None, 1, 0, None, None, 0, None) == mm.MUON_ERR_INVALID_ARG
+    g = (mm._Group * 1)()
+    g[0] = mm._Group(8, 8, 8, 1, 4, 4, 0, 16)
+    hp = mm.HParams().to_c()
+    # workspace missing
+    assert lib.muon_step(g, 1, mm.DTYPE_F32, ctypes.byref(hp), None, 0, None) == mm.MUON_ERR_WORKSPACE
+    assert lib.muon_step_workspace_size(g, 1) > 0
+    # bad batch stride
+    g[0] = mm._Group(8, 8, 8, 1, 4, 4, 0, 15)
+    assert lib.muon_step(g, 1, mm.DTYPE_F32, ctypes.byref(hp), None, 0, None) == mm.MUON_ERR_INVALID_ARG
+    assert lib.muon_step_workspace_size(g, 1) == 0
+    # zero rows, bad dtype, bad steps
+    g[0] = mm._Group(8, 8, 8, 1, 0, 4, 0, 16)
+    assert lib.muon_step(g, 1, mm.DTYPE_F32, ctypes.byref(hp), None, 0, None) == mm.MUON_ERR_INVALID_ARG
+    g[0] = mm._Group(8, 8, 8, 1, 4, 4, 0, 16)
+    assert lib.muon_step(g, 1, 7, ctypes.byref(hp), None, 0, None) == mm.MUON_ERR_INVALID_ARG
+    hp.ns_steps = 0
+    assert lib.muon_step(g, 1, mm.DTYPE_F32, ctypes.byref(hp), None, 0, None) == mm.MUON_ERR_INVALID_ARG
+    # QK-Clip argument checks
+    assert lib.qkclip_rowmax(16, 16, 1, 8, 2, 96, 0.1, 1, 16, 16, 1 << 20, None) == mm.MUON_ERR_UNSUPPORTED
+    assert lib.qkclip_rowmax(16, 16, 1, 8, 2, 64, 0.0, 1, 16, 16, 1 << 20, None) == mm.MUON_ERR_INVALID_ARG
+    assert lib.qkclip_rowmax(16, 16, 1, 8, 2, 64, 0.1, 1, 16, None, 0, None) == mm.MUON_ERR_WORKSPACE
+    assert lib.qkclip_rescale(None, 16, 1, 2, 64, 8, 16, 100.0, 0.5, None, None) == mm.MUON_ERR_INVALID_ARG
+    assert lib.qkclip_rescale(16, 16, 1, 2, 64, 8, 16, -1.0, 0.5, None, None) == mm.MUON_ERR_INVALID_ARG
+    assert lib.qkclip_rescale(16, 16, 1, 2, 64, 8, 16, 100.0, 1.5, None, None) == mm.MUON_ERR_INVALID_ARG
+    assert lib.ns_orthogonalize(16, 0, 16, 1, 4, 4, 16, 5, 3.4, -4.7, 2.0, 1e-7, None, 0, None) == mm.MUON_ERR_WORKSPACE
+    assert lib.ns_workspace_size(1, 0, 4) == 0
+
+
+def test_workspace_layout_query(lib):
+    import matrix_orthogonalizing_optimizer_muon_amd as mm
+    g = (mm._Group * 2)()
+    g[0] = mm._Group(8, 8, 8, 3, 300, 100, 0, 30000)   # tall
+    g[1] = mm._Group(8, 8, 8, 2, 100, 700, 0, 70000)   # wide, tile 128
+    lay = mm._WsLayout()
+    assert lib.muon_step_workspace_layout(g, 2, 0, 5, ctypes.byref(lay)) == 0
+    # tall: O is the transposed buffer, leading dimension = padded cols (128)
+    assert lay.o_ld == 128 and lay.x0_ld == 384
+    assert lay.o_offset % 256 == 0 and lay.inv_norm_offset % 256 == 0
+    assert lib.muon_step_workspace_layout(g, 2, 1, 4, ctypes.byref(lay)) == 0
+    assert lay.o_ld == 768 and lay.x0_ld == 768
+    assert lib.muon_step_workspace_layout(g, 2, 2, 5, ctypes.byref(lay)) == mm.MUON_ERR_INVALID_ARG
+    total = lib.muon_step_workspace_size(g, 2)
+    assert lay.o_offset < total
