@@ -252,14 +252,15 @@ GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b,
     q.Et = A; q.sEt = sa; q.lde = p.mp;
     q.tm = T; q.tn = T; q.sym = 1; q.tiles_per_mat = T * (T + 1) / 2;
     q.alpha_pow = 0;
-    q.c_acc = c; q.c_e = b; q.c_diag = a;
+    q.c_acc = c; q.c_e = b;
     q.mvalid = p.mp; q.nvalid = p.mp;
   } else {
     const int TN = p.np / p.tile;
     q.P = B; q.Q = Xt; q.sP = sa; q.sQ = sx; q.ldp = p.mp; q.ldq = p.mp; q.K = p.mp;
+    q.Et = Xt; q.sEt = sx; q.lde = p.mp;
     q.tm = T; q.tn = TN; q.sym = 0; q.tiles_per_mat = T * TN;
     q.alpha_pow = (t == 0) ? 1 : 0;
-    q.c_acc = 1.0f; q.c_e = 0.0f;
+    q.c_acc = 1.0f; q.c_e = a;
     const bool last = (t == steps - 1);
     if (!last) {
       q.C = Xn; q.sC = sx; q.ldc = p.np;
@@ -300,7 +301,7 @@ int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c,
         }
         if (L.nprob == 0) continue;
         L.prefix[L.nprob] = tiles;
-        MUON_LAUNCH(kinds[stage], s, launch_ns_gemm(L, tile, tiles, s));
+        MUON_LAUNCH(kinds[stage], s, launch_ns_gemm(L, tile, stage, tiles, s));
       }
     }
   }

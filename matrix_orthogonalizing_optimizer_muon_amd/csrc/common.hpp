@@ -160,7 +160,7 @@ struct UpdateLaunch {
 // Launchers (defined next to their kernels).  Each returns hipGetLastError().
 hipError_t launch_momentum_norm(const MomentumLaunch& L, int grad_dtype, int nblocks, hipStream_t s);
 hipError_t launch_norm_finalize(const FinalizeLaunch& L, int nmats, hipStream_t s);
-hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int nblocks, hipStream_t s);
+hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks, hipStream_t s);
 hipError_t launch_param_update(const UpdateLaunch& L, int param_dtype, int64_t nblocks, hipStream_t s);
 hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int H, int d_head,
                             int causal, float* partial, int nqb, hipStream_t s);

@@ -5,19 +5,25 @@
 //
 // Every product of the iteration is an "NT" contraction whose two operands
 // are row-major with the contraction index contiguous:
-//   A = X X^T                P = Q = X  (m x n),  K = n, symmetric output
-//   B = a I + b A + c A A^T  P = Q = A  (m x m),  K = m, symmetric output (A = A^T)
-//   X' = B X                 P = B,  Q = X^T (n x m), K = m
-// (a X + (b A + c A A) X is computed as (a I + b A + c A A) X: one rounding of
-// the polynomial matrix, no a X term in the last product.)
+//   A = X X^T            P = Q = X  (m x n),  K = n, symmetric output
+//   B = b A + c A A^T    P = Q = A  (m x m),  K = m, symmetric output (A = A^T)
+//   X' = a X + B X       P = B,  Q = X^T (n x m), K = m
+// The a X term is added in the epilogue from the stored bf16 X (read as X^T
+// rows): keeping it out of the bf16-rounded polynomial matrix B measured
+// about 4x lower Newton-Schulz error than rounding a I + b A + c A A.
 // so both MFMA operands are 16-byte row segments, staged through LDS.  The
 // symmetric products compute only tiles ti <= tj and write each off-diagonal
 // tile twice (in place and mirrored).  X is kept in both layouts (X and X^T):
 // the epilogue of X' writes both, so no transpose pass is ever needed.
 //
 // Tiling: TILE x TILE output per 256-thread block, 2 x 2 waves, each wave a
-// (TILE/2) x (TILE/2) sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16),
-// K staged 32 at a time in double-buffered, padded LDS.
+// (TILE/2) x (TILE/2) sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16).
+// K is staged 64 at a time: 16-byte buffer loads into registers one slice
+// ahead (full 128-byte row segments, the fastest tile-read pattern measured on
+// this chip), double-buffered LDS with rows padded to 144 bytes (conflict-free
+// 128-bit fragment reads), barriers without the workgroup fence so the
+// prefetch stays in flight, next-substep fragments read while the current
+// substep's MFMAs issue (ordering pinned with sched_group_barrier).
 #include <utility>
 
 #include "common.hpp"
@@ -88,7 +94,7 @@ __device__ __forceinline__ void epilogue_all(const f32x16_t (&acc)[F][F], const 
   (epilogue_block<Is / F, Is % F>(acc[Is / F][Is % F], e), ...);
 }
 
-template <int TILE>
+template <int TILE, int STAGE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_kernel(GemmLaunch L) {
   constexpr int WT = TILE / 2;       // wave sub-tile edge
@@ -141,76 +147,93 @@ void ns_gemm_kernel(GemmLaunch L) {
   const int lrow = tid / CPR;
   const int lkc = (tid % CPR) * 8;
 
-  const bf16_t* gP[NCH];
-  const bf16_t* gQ[NCH];
-  int sOff[NCH];
-  static_for<NCH>([&](auto c) {
-    const int row = lrow + RPP * c;
-    gP[c] = Pg + static_cast<int64_t>(row) * p.ldp + lkc;
-    gQ[c] = Qg + static_cast<int64_t>(row) * p.ldq + lkc;
-    sOff[c] = row * kPitch + lkc;
-  });
+  // global -> register staging through buffer loads: chunk c of this thread
+  // is tile row lrow + RPP*c, 16 bytes at column lkc of the K slice
+  const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc((void*)Pg, 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc((void*)Qg, 0, 0x7fffffff, 0x00020000);
+  const int vP = (lrow * p.ldp + lkc) * 2;
+  const int vQ = (lrow * p.ldq + lkc) * 2;
+  const int sstrP = RPP * p.ldp * 2, sstrQ = RPP * p.ldq * 2;
+  const int sOff = (lrow * kPitch + lkc) * 2;   // bytes inside an LDS stage
   u32x4_t rP[NCH], rQ[NCH];
+  const int KT = p.K / kBK;
+  auto gload = [&](int kslice) {
+    const int kb = min(kslice, KT - 1) * kBK * 2;
+    static_for<NCH>([&](auto c) {
+      rP[c] = __builtin_amdgcn_raw_buffer_load_b128(rsP, vP, kb + c * sstrP, 0);
+      rQ[c] = __builtin_amdgcn_raw_buffer_load_b128(rsQ, vQ, kb + c * sstrQ, 0);
+    });
+  };
+  auto sstore = [&](int buf) {
+    char* bP = reinterpret_cast<char*>(sP[buf]) + sOff;
+    char* bQ = reinterpret_cast<char*>(sQ[buf]) + sOff;
+    static_for<NCH>([&](auto c) {
+      *reinterpret_cast<u32x4_t*>(bP + c * RPP * kPitch * 2) = rP[c];
+      *reinterpret_cast<u32x4_t*>(bQ + c * RPP * kPitch * 2) = rQ[c];
+    });
+  };
+  // barrier without the workgroup fence of __syncthreads (that fence would
+  // drain the prefetch loads): this wave's LDS traffic done, then s_barrier
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+  };
 
   f32x16_t acc[F][F];
   static_for<F * F>([&](auto ab) { acc[ab / F][ab % F] = f32x16_t{}; });
 
-  const int KT = p.K / kBK;
-  static_for<NCH>([&](auto c) {
-    rP[c] = *reinterpret_cast<const u32x4_t*>(gP[c]);
-    rQ[c] = *reinterpret_cast<const u32x4_t*>(gQ[c]);
-  });
-  static_for<NCH>([&](auto c) {
-    *reinterpret_cast<u32x4_t*>(&sP[0][sOff[c]]) = rP[c];
-    *reinterpret_cast<u32x4_t*>(&sQ[0][sOff[c]]) = rQ[c];
-  });
-  __syncthreads();
+  const int frow = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  const int aoff = ((wr0 + frow) * kPitch + fk) * 2;
+  const int boff = ((wc0 + frow) * kPitch + fk) * 2;
+  bf16x8_t fa[2][F], fb[2][F];
+  auto read_frags = [&](int buf, int s, auto slot) {
+    const char* bP = reinterpret_cast<const char*>(sP[buf]) + aoff + s * 32;
+    const char* bQ = reinterpret_cast<const char*>(sQ[buf]) + boff + s * 32;
+    static_for<F>([&](auto a) { fa[slot][a] = *reinterpret_cast<const bf16x8_t*>(bP + a * 32 * kPitch * 2); });
+    static_for<F>([&](auto b) { fb[slot][b] = *reinterpret_cast<const bf16x8_t*>(bQ + b * 32 * kPitch * 2); });
+  };
+  auto mfmas = [&](auto slot) {
+    static_for<F * F>([&](auto ab) {
+      constexpr int A = decltype(ab)::value / F, B = decltype(ab)::value % F;
+      acc[A][B] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][A], fb[slot][B], acc[A][B], 0, 0, 0);
+    });
+  };
+  // interleave: per MFMA one LDS read (first 2F MFMAs), optionally global loads
+  auto pattern = [&](int nv, int nw) {
+    for (int q = 0; q < F * F; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < 2 * F) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (q < nw) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+  };
+  constexpr int S = kBK / 16;   // 4 K-substeps per slice
 
-  const int frow = lane & 31;        // fragment row inside a 32-block
-  const int fk = (lane >> 5) * 8;    // fragment K offset (0 or 8)
-
+  gload(0);
+  sstore(0);
+  gload(1);
+  barrier();
+  read_frags(0, 0, std::integral_constant<int, 0>{});
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int k1 = (kt + 1) * kBK;
-      static_for<NCH>([&](auto c) {
-        rP[c] = *reinterpret_cast<const u32x4_t*>(gP[c] + k1);
-        rQ[c] = *reinterpret_cast<const u32x4_t*>(gQ[c] + k1);
-      });
-    }
-    const bf16_t* sPc = sP[cur];
-    const bf16_t* sQc = sQ[cur];
-    // Fragments of K-substep s+1 are read from LDS before the MFMAs of
-    // substep s are issued, so LDS latency hides behind matrix work.
-    bf16x8_t fa[2][F], fb[2][F];
-    auto read_frags = [&](auto s, auto slot) {
-      static_for<F>([&](auto a) {
-        fa[slot][a] = *reinterpret_cast<const bf16x8_t*>(&sPc[(wr0 + a * 32 + frow) * kPitch + s * 16 + fk]);
-      });
-      static_for<F>([&](auto b) {
-        fb[slot][b] = *reinterpret_cast<const bf16x8_t*>(&sQc[(wc0 + b * 32 + frow) * kPitch + s * 16 + fk]);
-      });
-    };
-    read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    static_for<kBK / 16>([&](auto s) {
-      constexpr int S = decltype(s)::value;
-      constexpr int slot = S & 1;
-      if constexpr (S + 1 < kBK / 16)
-        read_frags(std::integral_constant<int, S + 1>{}, std::integral_constant<int, slot ^ 1>{});
-      static_for<F * F>([&](auto ab) {
-        constexpr int A = decltype(ab)::value / F, B = decltype(ab)::value % F;
-        acc[A][B] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][A], fb[slot][B], acc[A][B], 0, 0, 0);
-      });
+    static_for<S - 1>([&](auto s) {
+      constexpr int SS = decltype(s)::value;
+      read_frags(cur, SS + 1, std::integral_constant<int, (SS + 1) & 1>{});
+      if constexpr (SS == S - 2) {
+        // stage slice kt+1 (loaded one iteration ago), then prefetch kt+2
+        sstore(cur ^ 1);
+        gload(kt + 2);
+      }
+      mfmas(std::integral_constant<int, SS & 1>{});
+      pattern(SS == S - 2 ? 2 * NCH : 0, SS == S - 2 ? 2 * NCH : 0);
     });
-    if (more) {
-      static_for<NCH>([&](auto c) {
-        *reinterpret_cast<u32x4_t*>(&sP[cur ^ 1][sOff[c]]) = rP[c];
-        *reinterpret_cast<u32x4_t*>(&sQ[cur ^ 1][sOff[c]]) = rQ[c];
-      });
-    }
-    __syncthreads();
+    barrier();
+    read_frags(cur ^ 1, 0, std::integral_constant<int, 0>{});
+    mfmas(std::integral_constant<int, (S - 1) & 1>{});
+    pattern(0, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue.  Element e of acc[a][b] holds C[i][j] with
   //   i = tile_i0 + wr0 + 32 a + 8 (e / 4) + 4 (lane / 32) + (e % 4),
@@ -236,11 +259,17 @@ void ns_gemm_kernel(GemmLaunch L) {
 
 }  // namespace
 
-hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int nblocks, hipStream_t s) {
-  if (tile == 256)
-    hipLaunchKernelGGL(ns_gemm_kernel<256>, dim3(nblocks), dim3(256), 0, s, L);
-  else
-    hipLaunchKernelGGL(ns_gemm_kernel<128>, dim3(nblocks), dim3(256), 0, s, L);
+hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks, hipStream_t s) {
+  // one symbol per (tile, stage) so kernel traces attribute time per product
+  if (tile == 256) {
+    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<256, 0>), dim3(nblocks), dim3(256), 0, s, L);
+    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<256, 1>), dim3(nblocks), dim3(256), 0, s, L);
+    else hipLaunchKernelGGL((ns_gemm_kernel<256, 2>), dim3(nblocks), dim3(256), 0, s, L);
+  } else {
+    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<128, 0>), dim3(nblocks), dim3(256), 0, s, L);
+    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<128, 1>), dim3(nblocks), dim3(256), 0, s, L);
+    else hipLaunchKernelGGL((ns_gemm_kernel<128, 2>), dim3(nblocks), dim3(256), 0, s, L);
+  }
   return hipGetLastError();
 }
 
