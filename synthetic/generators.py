@@ -281,3 +281,22 @@ def qk_inputs_torch(seed, batch, seq, heads, d_head, d_model, designated, target
         Wq[h * d_head:(h + 1) * d_head] *= s
         Wk[h * d_head:(h + 1) * d_head] *= s
     return dict(X=X, Wq=Wq.to(torch.bfloat16), Wk=Wk.to(torch.bfloat16), designated_heads=heads_sel)
+
+
+def lowrank_torch(rows, cols, seed, device, rank=32, decay=1.5, noise_std=0.01, magnitude=1.0):
+    """low_rank_plus_noise drawn for the GPU: orthonormal factors from NumPy QR
+    of seeded Gaussians (host), the rank-r product and the N(0, noise_std^2)
+    noise on the device, times `magnitude`, cast to bf16."""
+    import torch
+    g = rng(seed)
+    r = min(rank, rows, cols)
+    Ur, _ = np.linalg.qr(g.standard_normal((rows, r)))
+    Vr, _ = np.linalg.qr(g.standard_normal((cols, r)))
+    s = np.arange(1, r + 1, dtype=np.float64) ** (-decay)
+    U = torch.from_numpy((Ur * s).astype(np.float32)).to(device)
+    V = torch.from_numpy(Vr.astype(np.float32)).to(device)
+    G = U @ V.t()
+    G += bulk_normal_torch((rows, cols), noise_std, seed + 1, device, torch.float32)
+    if magnitude != 1.0:
+        G *= magnitude
+    return G.to(torch.bfloat16)

@@ -1,0 +1,215 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses (all groups of a workload in one muon_step call).
+
+Outputs the oracle can afford are compared whole (workload 2: every matrix);
+for the large workloads the oracle recomputes sampled matrices one by one
+(every shape class is sampled).  Inputs of workloads 3 and 4 are drawn on the
+GPU by torch's seeded generator and copied back for the sampled matrices;
+workloads 2 and 5 are drawn on the host.  Tolerances as in test_gpu_parity.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import muon_oracle as O
+from synthetic import generators as gen
+from tests.gpu_util import rel_fro, to_dev, to_host
+from tests.test_gpu_parity import w_excess
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import matrix_orthogonalizing_optimizer_muon_amd as m
+    m.load_library()
+    return m
+
+
+def hp_of(mm, wl):
+    return mm.HParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay,
+                      nesterov=wl.nesterov, ns_steps=wl.ns_steps, ns_coeffs=wl.ns_coeffs,
+                      ns_eps=wl.ns_eps, rms_target=wl.rms_target)
+
+
+def check_matrix(tag, W0, M0, G0, Wg, Mg, Og, hp, rows, cols, dtype):
+    """One matrix: momentum (fp32, 1e-5), Newton-Schulz (2e-2), update given
+    the GPU's own O (faithful bf16 / 1e-5 fp32)."""
+    wide = (lambda a: O.bf16_bits_to_f64(a)) if dtype == "bf16" else (lambda a: np.asarray(a, np.float64))
+    Gf = wide(G0)
+    Mr = O.momentum_update(np.asarray(M0, np.float64), Gf, hp.momentum)
+    U = O.nesterov_lookahead(Mr, Gf, hp.momentum, hp.nesterov)
+    em = rel_fro(Mg, Mr)
+    Or = O.newton_schulz(U, hp.ns_steps, *hp.ns_coeffs, eps=hp.ns_eps)
+    eo = rel_fro(Og, Or)
+    s = O.update_scale(rows, cols, hp.scale_mode, hp.rms_target)
+    Wr = O.param_update(wide(W0), Og, hp.lr, hp.weight_decay, s)
+    if dtype == "bf16":
+        ew = w_excess(Wg, Wr, wide(W0), Og, hp, s)
+        wok = ew == 0
+    else:
+        ew = rel_fro(Wg, Wr)
+        wok = ew <= 1e-5
+    say(f"   {tag} [{rows}x{cols}]: M {em:.2e} O {eo:.3e} W {ew}")
+    assert em <= 1e-5 and eo <= 2e-2 and wok
+
+
+def test_workload2_one_layer_hidden_2048(mm):
+    """Workload 2: one transformer layer, hidden 2048 (4 x 2048^2, 2 x 8192x2048,
+    1 x 2048x8192), bf16 params, fp32 momentum, low-rank-plus-noise gradients.
+    Every matrix is checked against the oracle."""
+    import torch
+    say("[workload 2] one layer, hidden 2048")
+    wl = gen.workload(2)
+    dev = torch.device("cuda:0")
+    host, devg = [], []
+    for gi in range(len(wl.groups)):
+        W, M, G = gen.group_params(wl, gi, 2), gen.group_momentum(wl, gi, 2), gen.group_grads(wl, gi, 2)
+        host.append((W, M, G))
+        devg.append((to_dev(W, dev), to_dev(G, dev), to_dev(M, dev)))
+    hp = hp_of(mm, wl)
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    for gi, grp in enumerate(wl.groups):
+        o, _, _ = mm.workspace_views(devg, gi, ws, hp.ns_steps)
+        Og = O.bf16_bits_to_f64(to_host(o))
+        Wg, Mg = to_host(devg[gi][0]), to_host(devg[gi][2])
+        for b in range(grp.batch):
+            check_matrix(f"{grp.name}#{b}", host[gi][0][b], host[gi][1][b], host[gi][2][b],
+                         Wg[b], Mg[b], Og[b], hp, grp.rows, grp.cols, "bf16")
+
+
+def gpu_groups(wl, seed, dev, lowrank=False):
+    """Draw a large workload on the GPU: W ~ N(0, 0.02^2) bf16, M ~ 0.5 N(0,1)
+    fp32, G bf16 (N(0,1), or low-rank-plus-noise per matrix with an optional
+    Zipf magnitude)."""
+    import torch
+    out = []
+    for gi, grp in enumerate(wl.groups):
+        shape = (grp.batch, grp.rows, grp.cols)
+        W = gen.bulk_normal_torch(shape, wl.weight_std, seed * 100 + gi, dev, torch.bfloat16)
+        M = gen.bulk_normal_torch(shape, 0.5, seed * 100 + 50 + gi, dev, torch.float32)
+        if not lowrank:
+            G = gen.bulk_normal_torch(shape, 1.0, seed * 100 + 10 + gi, dev, torch.bfloat16)
+        else:
+            mags = gen.zipf_magnitudes(gen.rng(seed * 7 + 3 + gi), grp.batch) \
+                if wl.grad_kind == "lowrank_zipf" else np.ones(grp.batch)
+            G = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+            for e in range(grp.batch):
+                G[e] = gen.lowrank_torch(grp.rows, grp.cols, seed * 10000 + gi * 1000 + e, dev,
+                                         magnitude=float(mags[e]))
+        out.append((W, G, M))
+    return out
+
+
+def run_sampled(mm, wl, devg, samples):
+    import torch
+    host = {gi: {b: (to_host(devg[gi][0][b]), to_host(devg[gi][2][b]), to_host(devg[gi][1][b]))
+                 for b in bs} for gi, bs in samples.items()}
+    hp = hp_of(mm, wl)
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    for gi, bs in samples.items():
+        grp = wl.groups[gi]
+        o, _, _ = mm.workspace_views(devg, gi, ws, hp.ns_steps)
+        for b in bs:
+            W0, M0, G0 = host[gi][b]
+            check_matrix(f"{grp.name}#{b}", W0, M0, G0, to_host(devg[gi][0][b]), to_host(devg[gi][2][b]),
+                         O.bf16_bits_to_f64(to_host(o[b])), hp, grp.rows, grp.cols, "bf16")
+
+
+def test_workload3_dense_decoder_24_layers(mm):
+    """Workload 3: 24-layer decoder Muon group, hidden 4096 (48 x 4096^2,
+    48 x 1024x4096, 48 x 14336x4096, 24 x 4096x14336), one call; one sampled
+    matrix per shape class, plus the last matrix of the largest class."""
+    import torch
+    say("[workload 3] 24 layers, hidden 4096")
+    wl = gen.workload(3)
+    devg = gpu_groups(wl, 3, torch.device("cuda:0"))
+    run_sampled(mm, wl, devg, {0: [17], 1: [47], 2: [5], 3: [23]})
+
+
+def test_workload4_moe_64_experts(mm):
+    """Workload 4: 64-expert MoE (128 x 2048x7168 up/gate, 64 x 7168x2048
+    down), low-rank-plus-noise gradients with a Zipf(1.1) magnitude per
+    expert; sampled experts per shape class, including the smallest magnitude."""
+    import torch
+    say("[workload 4] 64 experts")
+    wl = gen.workload(4)
+    devg = gpu_groups(wl, 4, torch.device("cuda:0"), lowrank=True)
+    mags0 = gen.zipf_magnitudes(gen.rng(4 * 7 + 3 + 0), 128)
+    mags1 = gen.zipf_magnitudes(gen.rng(4 * 7 + 3 + 1), 64)
+    run_sampled(mm, wl, devg, {0: [int(np.argmin(mags0)), 3], 1: [int(np.argmax(mags1)), 40]})
+
+
+def test_workload5_muonclip_layer(mm):
+    """Workload 5 exactly as the benchmark runs it: per-head S_max on the
+    forward's Q, K [4, 4096, 64, 128] (all 64 heads against the oracle), the
+    Muon step on W_q, W_k, W_v [8192x7168] and W_o [7168x8192] (sampled
+    matrices), then the per-head rescale; clip flags bit-exact."""
+    import torch
+    say("[workload 5] MuonClip layer")
+    wl = gen.workload(5)
+    ex = wl.extra
+    B, T, H, D, dm = ex["batch"], ex["seq"], ex["heads"], ex["d_head"], ex["d_model"]
+    dev = torch.device("cuda:0")
+    qk = gen.qk_inputs(55, B, T, H, D, dm, ex["n_designated"], ex["targets"])
+    say("   projecting Q, K on the host")
+    Qb = gen.project_host(qk["X"], qk["Wq"]).reshape(B, T, H, D)
+    Kb = gen.project_host(qk["X"], qk["Wk"]).reshape(B, T, H, D)
+    Wqkv = np.stack([qk["Wq"], qk["Wk"], gen.group_params(wl, 0, 5)[2]])
+    Wo = gen.group_params(wl, 1, 5)
+    Mqkv, Mo = gen.group_momentum(wl, 0, 5), gen.group_momentum(wl, 1, 5)
+    Gqkv, Go = gen.group_grads(wl, 0, 5), gen.group_grads(wl, 1, 5)
+    devg = [(to_dev(Wqkv, dev), to_dev(Gqkv, dev), to_dev(Mqkv, dev)),
+            (to_dev(Wo, dev), to_dev(Go, dev), to_dev(Mo, dev))]
+    hp = hp_of(mm, wl)
+    s_dev = mm.qkclip_rowmax(to_dev(Qb, dev), to_dev(Kb, dev), 1 / math.sqrt(D), True)
+    ws = mm.muon_step(devg, hp)
+    o, _, _ = mm.workspace_views(devg, 0, ws, hp.ns_steps)
+    Wq_mid = to_host(devg[0][0][0]).copy()   # after the Muon step, before the clip
+    Wk_mid = to_host(devg[0][0][1]).copy()
+    flags = mm.qkclip_rescale(devg[0][0][0], devg[0][0][1], s_dev, D, ex["tau"], ex["alpha"])
+    torch.cuda.synchronize()
+    s_gpu = to_host(s_dev).astype(np.float64)
+    say("   oracle S_max over all heads")
+    s_ref = O.smax_per_head(O.bf16_bits_to_f64(Qb), O.bf16_bits_to_f64(Kb), 1 / math.sqrt(D), True)
+    err = np.abs(s_gpu - s_ref) / np.abs(s_ref)
+    say(f"   S_max max rel err {err.max():.2e}; designated {sorted(qk['designated_heads'].tolist())}")
+    assert err.max() <= 1e-5
+    _, fl_ref = O.qkclip_factors(s_ref, ex["tau"])
+    assert list(to_host(flags)) == list(fl_ref)
+    assert set(np.nonzero(fl_ref == 1)[0].tolist()) == set(qk["designated_heads"].tolist())
+    assert s_ref[qk["designated_heads"]].min() >= 1.1 * ex["tau"]
+    others = np.setdiff1d(np.arange(H), qk["designated_heads"])
+    assert s_ref[others].max() <= ex["tau"] / 5
+    # rescale of the clipped heads on the post-step weights
+    for Wmid, gidx, expo in ((Wq_mid, 0, ex["alpha"]), (Wk_mid, 1, 1 - ex["alpha"])):
+        got = O.bf16_bits_to_f64(to_host(devg[0][0][gidx]))
+        for h in range(H):
+            rows = slice(h * D, (h + 1) * D)
+            if fl_ref[h] == 1:
+                f = (ex["tau"] / s_gpu[h]) ** expo
+                exact = O.bf16_bits_to_f64(Wmid[rows]) * f
+                x = got[rows]
+                _, e = np.frexp(np.abs(x))
+                bound = np.ldexp(1.0, e - 9) + 2.0 ** -22 * np.abs(exact)
+                assert np.all(np.abs(x - exact) <= bound * (1 + 1e-12))
+            else:
+                assert np.array_equal(to_host(devg[0][0][gidx])[rows], Wmid[rows])
+    # sampled Muon matrices: W_v (tall class, never rescaled) and W_o (wide)
+    b = 2
+    check_matrix("W_v", Wqkv[b], Mqkv[b], Gqkv[b], to_host(devg[0][0][b]), to_host(devg[0][2][b]),
+                 O.bf16_bits_to_f64(to_host(o[b])), hp, 8192, 7168, "bf16")
+    o1, _, _ = mm.workspace_views(devg, 1, ws, hp.ns_steps)
+    check_matrix("W_o", Wo[0], Mo[0], Go[0], to_host(devg[1][0][0]), to_host(devg[1][2][0]),
+                 O.bf16_bits_to_f64(to_host(o1[0])), hp, 7168, 8192, "bf16")
