@@ -51,57 +51,9 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(MomentumLaunch L) {
   const float mu = L.mu;
   double ss = 0.0;
 
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = rsub + 16 * p;
-    const int i = i0 + r;
-    float u[4];
-    if (i < g.rows && g.vec && j0 + c0 + 3 < g.cols) {
-      const int64_t e = static_cast<int64_t>(i) * g.cols + j0 + c0;
-      float gv[4];
-      if constexpr (sizeof(GT) == 2) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(G + e);
-        gv[0] = bf16_to_f32(raw.x & 0xffff);
-        gv[1] = bf16_to_f32(raw.x >> 16);
-        gv[2] = bf16_to_f32(raw.y & 0xffff);
-        gv[3] = bf16_to_f32(raw.y >> 16);
-      } else {
-        const float4 raw = *reinterpret_cast<const float4*>(G + e);
-        gv[0] = raw.x; gv[1] = raw.y; gv[2] = raw.z; gv[3] = raw.w;
-      }
-      if (M) {
-        float4 mv = *reinterpret_cast<const float4*>(M + e);
-        float m[4] = {mv.x, mv.y, mv.z, mv.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          m[q] = fmaf(mu, m[q], gv[q]);
-          u[q] = L.nesterov ? fmaf(mu, m[q], gv[q]) : m[q];
-        }
-        *reinterpret_cast<float4*>(M + e) = make_float4(m[0], m[1], m[2], m[3]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) u[q] = gv[q];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + c0 + q;
-        u[q] = 0.0f;
-        if (i < g.rows && j < g.cols) {
-          const int64_t e = static_cast<int64_t>(i) * g.cols + j;
-          float gv;
-          if constexpr (sizeof(GT) == 2) gv = bf16_to_f32(reinterpret_cast<const bf16_t*>(G)[e]);
-          else gv = static_cast<float>(G[e]);
-          if (M) {
-            const float m = fmaf(mu, M[e], gv);
-            M[e] = m;
-            u[q] = L.nesterov ? fmaf(mu, m, gv) : m;
-          } else {
-            u[q] = gv;
-          }
-        }
-      }
-    }
+  // stores U of one 4-element row segment (own layout + the LDS tile for the
+  // transposed copy) and accumulates its squares
+  auto emit = [&](int r, const float (&u)[4]) {
     bf16_t ub[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -109,11 +61,81 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(MomentumLaunch L) {
       ub[q] = f32_to_bf16(u[q]);
       tr[(c0 + q) * kTrPitch + r] = ub[q];
     }
-    // U in its own layout (padded extent always written).
     uint2 packed;
     packed.x = static_cast<uint32_t>(ub[0]) | (static_cast<uint32_t>(ub[1]) << 16);
     packed.y = static_cast<uint32_t>(ub[2]) | (static_cast<uint32_t>(ub[3]) << 16);
-    *reinterpret_cast<uint2*>(D1 + static_cast<int64_t>(i) * g.cp + j0 + c0) = packed;
+    *reinterpret_cast<uint2*>(D1 + static_cast<int64_t>(i0 + r) * g.cp + j0 + c0) = packed;
+  };
+
+  const bool interior = g.vec && (i0 + kTile <= g.rows) && (j0 + kTile <= g.cols);
+  if (interior) {
+    // whole tile inside the matrix: issue every load first (16 loads per
+    // thread in flight), then compute and store
+    float gv[4][4], mv[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int64_t e = static_cast<int64_t>(i0 + rsub + 16 * p) * g.cols + j0 + c0;
+      if constexpr (sizeof(GT) == 2) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(G + e);
+        gv[p][0] = bf16_to_f32(raw.x & 0xffff);
+        gv[p][1] = bf16_to_f32(raw.x >> 16);
+        gv[p][2] = bf16_to_f32(raw.y & 0xffff);
+        gv[p][3] = bf16_to_f32(raw.y >> 16);
+      } else {
+        const float4 raw = *reinterpret_cast<const float4*>(G + e);
+        gv[p][0] = raw.x; gv[p][1] = raw.y; gv[p][2] = raw.z; gv[p][3] = raw.w;
+      }
+      if (M) {
+        const float4 m4 = *reinterpret_cast<const float4*>(M + e);
+        mv[p][0] = m4.x; mv[p][1] = m4.y; mv[p][2] = m4.z; mv[p][3] = m4.w;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = rsub + 16 * p;
+      float u[4];
+      if (M) {
+        float mn[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          mn[q] = fmaf(mu, mv[p][q], gv[p][q]);
+          u[q] = L.nesterov ? fmaf(mu, mn[q], gv[p][q]) : mn[q];
+        }
+        const int64_t e = static_cast<int64_t>(i0 + r) * g.cols + j0 + c0;
+        f32x4_t mo = {mn[0], mn[1], mn[2], mn[3]};
+        __builtin_nontemporal_store(mo, reinterpret_cast<f32x4_t*>(M + e));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) u[q] = gv[p][q];
+      }
+      emit(r, u);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = rsub + 16 * p;
+      const int i = i0 + r;
+      float u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + c0 + q;
+        u[q] = 0.0f;
+        if (i < g.rows && j < g.cols) {
+          const int64_t e = static_cast<int64_t>(i) * g.cols + j;
+          float gvs;
+          if constexpr (sizeof(GT) == 2) gvs = bf16_to_f32(reinterpret_cast<const bf16_t*>(G)[e]);
+          else gvs = static_cast<float>(G[e]);
+          if (M) {
+            const float mn = fmaf(mu, M[e], gvs);
+            M[e] = mn;
+            u[q] = L.nesterov ? fmaf(mu, mn, gvs) : mn;
+          } else {
+            u[q] = gvs;
+          }
+        }
+      }
+      emit(r, u);
+    }
   }
 
   ss = wave_sum(ss);
@@ -139,20 +161,32 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(MomentumLaunch L) {
   }
 }
 
-// One block per matrix: fixed-order sum of the tile partials, then
-// 1 / (sqrt(sum) + eps).
-__global__ __launch_bounds__(64) void norm_finalize_kernel(FinalizeLaunch L) {
+// One block per matrix: fixed-order sum of the tile partials (each thread a
+// strided slice, four independent accumulators so the loads overlap, then a
+// fixed tree over threads), then 1 / (sqrt(sum) + eps).
+__global__ __launch_bounds__(256) void norm_finalize_kernel(FinalizeLaunch L) {
+  __shared__ double red[4];
   const int blk = blockIdx.x;
   int gi = 0;
   while (gi + 1 < L.ngroups && blk >= L.prefix[gi + 1]) ++gi;
   const int mat = blk - L.prefix[gi];
   const int n = L.tiles_per_mat[gi];
   const double* p = L.partials[gi] + static_cast<int64_t>(mat) * n;
-  double s = 0.0;
-  for (int k = threadIdx.x; k < n; k += 64) s += p[k];
-  s = wave_sum(s);
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int k = threadIdx.x;
+  for (; k + 768 < n; k += 1024) {
+    s0 += p[k];
+    s1 += p[k + 256];
+    s2 += p[k + 512];
+    s3 += p[k + 768];
+  }
+  for (; k < n; k += 256) s0 += p[k];
+  double s = wave_sum((s0 + s1) + (s2 + s3));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
   if (threadIdx.x == 0) {
-    L.inv_norm[gi][mat] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(L.eps)));
+    const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    L.inv_norm[gi][mat] = static_cast<float>(1.0 / (sqrt(tot) + static_cast<double>(L.eps)));
   }
 }
 
@@ -226,7 +260,7 @@ hipError_t launch_momentum_norm(const MomentumLaunch& L, int grad_dtype, int nbl
 }
 
 hipError_t launch_norm_finalize(const FinalizeLaunch& L, int nmats, hipStream_t s) {
-  hipLaunchKernelGGL(norm_finalize_kernel, dim3(nmats), dim3(64), 0, s, L);
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(nmats), dim3(256), 0, s, L);
   return hipGetLastError();
 }
 

@@ -5,25 +5,19 @@
 //
 // Every product of the iteration is an "NT" contraction whose two operands
 // are row-major with the contraction index contiguous:
-//   A = X X^T            P = Q = X  (m x n),  K = n, symmetric output
-//   B = b A + c A A^T    P = Q = A  (m x m),  K = m, symmetric output (A = A^T)
-//   X' = a X + B X       P = B,  Q = X^T (n x m), K = m
-// The a X term is added in the epilogue from the stored bf16 X (read as X^T
-// rows): keeping it out of the bf16-rounded polynomial matrix B measured
-// about 4x lower Newton-Schulz error than rounding a I + b A + c A A.
+//   A = X X^T                P = Q = X  (m x n),  K = n, symmetric output
+//   B = a I + b A + c A A^T  P = Q = A  (m x m),  K = m, symmetric output (A = A^T)
+//   X' = B X                 P = B,  Q = X^T (n x m), K = m
+// (a X + (b A + c A A) X is computed as (a I + b A + c A A) X: one rounding of
+// the polynomial matrix, no a X term in the last product.)
 // so both MFMA operands are 16-byte row segments, staged through LDS.  The
 // symmetric products compute only tiles ti <= tj and write each off-diagonal
 // tile twice (in place and mirrored).  X is kept in both layouts (X and X^T):
 // the epilogue of X' writes both, so no transpose pass is ever needed.
 //
 // Tiling: TILE x TILE output per 256-thread block, 2 x 2 waves, each wave a
-// (TILE/2) x (TILE/2) sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16).
-// K is staged 64 at a time: 16-byte buffer loads into registers one slice
-// ahead (full 128-byte row segments, the fastest tile-read pattern measured on
-// this chip), double-buffered LDS with rows padded to 144 bytes (conflict-free
-// 128-bit fragment reads), barriers without the workgroup fence so the
-// prefetch stays in flight, next-substep fragments read while the current
-// substep's MFMAs issue (ordering pinned with sched_group_barrier).
+// (TILE/2) x (TILE/2) sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16),
+// K staged 32 at a time in double-buffered, padded LDS.
 #include <utility>
 
 #include "common.hpp"
@@ -88,19 +82,22 @@ __device__ __forceinline__ void epilogue_block(const f32x16_t& acc, const EpiArg
   }
 }
 
-template <int F, int... Is>
-__device__ __forceinline__ void epilogue_all(const f32x16_t (&acc)[F][F], const EpiArgs& e,
+template <int F, int G, int... Is>
+__device__ __forceinline__ void epilogue_all(const f32x16_t (&acc)[F][G], const EpiArgs& e,
                                              std::integer_sequence<int, Is...>) {
-  (epilogue_block<Is / F, Is % F>(acc[Is / F][Is % F], e), ...);
+  (epilogue_block<Is / G, Is % G>(acc[Is / G][Is % G], e), ...);
 }
 
 template <int TILE, int STAGE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gemm_kernel(GemmLaunch L) {
-  constexpr int WT = TILE / 2;       // wave sub-tile edge
-  constexpr int F = WT / 32;         // 32x32 MFMA blocks per wave edge
+  constexpr int NT = 512;
+  constexpr int WT = TILE / 2;       // wave sub-tile rows
+  constexpr int WN = TILE / 4;       // wave sub-tile cols
+  constexpr int F = WT / 32;         // 32x32 MFMA blocks along rows
+  constexpr int G = WN / 32;         // along cols
   constexpr int CPR = kBK / 8;        // 16-byte chunks per tile row of a K slice
-  constexpr int RPP = 256 / CPR;      // tile rows covered by one pass of 256 threads
+  constexpr int RPP = NT / CPR;       // tile rows covered by one pass of the block
   constexpr int NCH = TILE / RPP;     // passes (chunks per thread per operand)
   static_assert(TILE % RPP == 0, "staging map must cover the tile exactly");
 
@@ -117,12 +114,35 @@ void ns_gemm_kernel(GemmLaunch L) {
   int t = local - mat * p.tiles_per_mat;
   int ti, tj;
   if (p.sym) {
-    ti = 0;
-    int rowlen = p.tm;
-    while (t >= rowlen) { t -= rowlen; ++ti; --rowlen; }
-    tj = ti + t;
+    {
+      constexpr int SB = 8;
+      // super-blocks of SB x SB tiles over the upper triangle, row-major over
+      // super-blocks; inside a super-block column-major (upper part only on the
+      // diagonal super-blocks)
+      const int nsb = (p.tm + SB - 1) / SB;
+      int bi = 0, bj = 0, found = 0;
+      for (bi = 0; bi < nsb && !found; ++bi) {
+        for (bj = bi; bj < nsb; ++bj) {
+          const int r0 = bi * SB, c0 = bj * SB;
+          const int rn = min(SB, p.tm - r0), cn = min(SB, p.tm - c0);
+          int cnt = 0;
+          if (bi == bj) cnt = rn * (rn + 1) / 2; else cnt = rn * cn;
+          if (t < cnt) {
+            if (bi == bj) {
+              int cc = 0;
+              while (t >= cc + 1) { t -= cc + 1; ++cc; }   // column cc holds rows 0..cc
+              ti = r0 + t; tj = c0 + cc;
+            } else {
+              ti = r0 + t % rn; tj = c0 + t / rn;
+            }
+            found = 1;
+            break;
+          }
+          t -= cnt;
+        }
+      }
+    }
   } else {
-    // groups of 8 tile-rows, column-major inside a group
     constexpr int GM = 8;
     const int gsz = GM * p.tn;
     const int grp = t / gsz;
@@ -139,8 +159,8 @@ void ns_gemm_kernel(GemmLaunch L) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr0 = (wave >> 1) * WT;  // wave row offset in the tile
-  const int wc0 = (wave & 1) * WT;   // wave col offset in the tile
+  const int wr0 = (wave >> 2) * WT;  // wave row offset in the tile
+  const int wc0 = (wave & 3) * WN;   // wave col offset in the tile
 
   // global -> register staging map: chunk c of this thread covers tile row
   // (tid / CPR + RPP * c), 8 bf16 at column 8 * (tid % CPR) of the K slice.
@@ -179,31 +199,31 @@ void ns_gemm_kernel(GemmLaunch L) {
     __builtin_amdgcn_s_barrier();
   };
 
-  f32x16_t acc[F][F];
-  static_for<F * F>([&](auto ab) { acc[ab / F][ab % F] = f32x16_t{}; });
+  f32x16_t acc[F][G];
+  static_for<F * G>([&](auto ab) { acc[ab / G][ab % G] = f32x16_t{}; });
 
   const int frow = lane & 31;
   const int fk = (lane >> 5) * 8;
   const int aoff = ((wr0 + frow) * kPitch + fk) * 2;
   const int boff = ((wc0 + frow) * kPitch + fk) * 2;
-  bf16x8_t fa[2][F], fb[2][F];
+  bf16x8_t fa[2][F], fb[2][G];
   auto read_frags = [&](int buf, int s, auto slot) {
     const char* bP = reinterpret_cast<const char*>(sP[buf]) + aoff + s * 32;
     const char* bQ = reinterpret_cast<const char*>(sQ[buf]) + boff + s * 32;
     static_for<F>([&](auto a) { fa[slot][a] = *reinterpret_cast<const bf16x8_t*>(bP + a * 32 * kPitch * 2); });
-    static_for<F>([&](auto b) { fb[slot][b] = *reinterpret_cast<const bf16x8_t*>(bQ + b * 32 * kPitch * 2); });
+    static_for<G>([&](auto b) { fb[slot][b] = *reinterpret_cast<const bf16x8_t*>(bQ + b * 32 * kPitch * 2); });
   };
   auto mfmas = [&](auto slot) {
-    static_for<F * F>([&](auto ab) {
-      constexpr int A = decltype(ab)::value / F, B = decltype(ab)::value % F;
+    static_for<F * G>([&](auto ab) {
+      constexpr int A = decltype(ab)::value / G, B = decltype(ab)::value % G;
       acc[A][B] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][A], fb[slot][B], acc[A][B], 0, 0, 0);
     });
   };
   // interleave: per MFMA one LDS read (first 2F MFMAs), optionally global loads
   auto pattern = [&](int nv, int nw) {
-    for (int q = 0; q < F * F; ++q) {
+    for (int q = 0; q < F * G; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < 2 * F) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < F + G) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (q < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (q < nw) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
@@ -254,21 +274,22 @@ void ns_gemm_kernel(GemmLaunch L) {
   e.mvalid = p.mvalid; e.nvalid = p.nvalid; e.ct_vec = p.ct_vec;
   e.i0 = ti * TILE + wr0 + 4 * (lane >> 5);
   e.j0 = tj * TILE + wc0 + (lane & 31);
-  epilogue_all<F>(acc, e, std::make_integer_sequence<int, F * F>{});
+  epilogue_all<F, G>(acc, e, std::make_integer_sequence<int, F * G>{});
 }
 
 }  // namespace
 
 hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks, hipStream_t s) {
   // one symbol per (tile, stage) so kernel traces attribute time per product
+  const dim3 grid(nblocks), block(512);
   if (tile == 256) {
-    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<256, 0>), dim3(nblocks), dim3(256), 0, s, L);
-    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<256, 1>), dim3(nblocks), dim3(256), 0, s, L);
-    else hipLaunchKernelGGL((ns_gemm_kernel<256, 2>), dim3(nblocks), dim3(256), 0, s, L);
+    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<256, 0>), grid, block, 0, s, L);
+    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<256, 1>), grid, block, 0, s, L);
+    else hipLaunchKernelGGL((ns_gemm_kernel<256, 2>), grid, block, 0, s, L);
   } else {
-    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<128, 0>), dim3(nblocks), dim3(256), 0, s, L);
-    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<128, 1>), dim3(nblocks), dim3(256), 0, s, L);
-    else hipLaunchKernelGGL((ns_gemm_kernel<128, 2>), dim3(nblocks), dim3(256), 0, s, L);
+    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<128, 0>), grid, block, 0, s, L);
+    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<128, 1>), grid, block, 0, s, L);
+    else hipLaunchKernelGGL((ns_gemm_kernel<128, 2>), grid, block, 0, s, L);
   }
   return hipGetLastError();
 }

@@ -9,9 +9,9 @@
 // balanced rescale; "About Muon: Muon At Scale", "When Softmax Collapses").
 //
 // The statistic is a causal Q K^T contraction reduced by max, so it runs as
-// a flash-style MFMA loop: one block per (batch row, head, 256 queries), the
-// queries' fragments held in registers, 64-key blocks staged through LDS,
-// the logits never stored.  Maxima are reduced across the wavefront with
+// a flash-style MFMA loop: one block per (batch row, head, 512 queries), the
+// queries' fragments held in registers, 64-key blocks (128 for d = 64)
+// staged through LDS, the logits never stored.  Maxima are reduced across the wavefront with
 // cross-lane max, across the block through LDS, and across blocks by a
 // second, fixed-order kernel (no atomics, no initialisation pass).
 #include "common.hpp"
@@ -20,8 +20,8 @@ namespace muon {
 
 namespace {
 
-constexpr int kQB = 256;   // queries per block (4 waves x 64)
-constexpr int kKB = 64;    // keys per LDS stage
+constexpr int kQB = 512;   // queries per block (8 waves x 64)
+constexpr int kThreads = 512;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -29,17 +29,27 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// One block = 512 consecutive queries of one (batch row, head); 8 waves of
+// 64 query rows, two per SIMD.  The queries' fragments stay in registers for
+// the whole key sweep; KB keys at a time are staged through double-buffered
+// LDS (registers one stage ahead, barrier without the workgroup fence so the
+// prefetch stays in flight).  Logits are reduced by max in registers; only
+// blocks on the causal diagonal (or the ragged tail) evaluate the mask.
 template <int D>
-__global__ __launch_bounds__(256) void qk_rowmax_kernel(const bf16_t* __restrict__ Q,
-                                                        const bf16_t* __restrict__ K, int B,
-                                                        int T, int H, int causal,
-                                                        float* __restrict__ partial, int nqb) {
-  constexpr int PITCH = D + 8;           // padded LDS row, bf16 units
-  constexpr int KS = D / 16;             // MFMA K-substeps
-  constexpr int NCH = kKB * (D / 8) / 256;  // 16-byte chunks per thread per key block
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][kKB * PITCH];
-  __shared__ float wmax[4];
-  __shared__ int wnan[4];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, int B,
+                      int T, int H, int causal, float* __restrict__ partial, int nqb) {
+  constexpr int KB = (D == 64) ? 128 : 64;    // keys per LDS stage
+  constexpr int NB = KB / 32;                 // 32-key MFMA blocks per stage
+  constexpr int PITCH = D + 8;                // padded LDS row, bf16 units
+  constexpr int KS = D / 16;                  // MFMA K-substeps
+  constexpr int CPR = D / 8;                  // 16-byte chunks per key row
+  constexpr int RPP = kThreads / CPR;         // key rows per pass
+  constexpr int NCH = KB / RPP;               // chunks per thread per stage
+  static_assert(KB % RPP == 0, "staging map must cover the stage exactly");
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KB * PITCH];
+  __shared__ float wmax[8];
+  __shared__ int wnan[8];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / nqb;
@@ -54,40 +64,35 @@ __global__ __launch_bounds__(256) void qk_rowmax_kernel(const bf16_t* __restrict
   const int r0 = qb * kQB + wave * 64;  // first query row of this wave
   const int frow = lane & 31, fk = (lane >> 5) * 8;
 
-  // Query fragments for the wave's 64 rows: [row block 0/1][K-substep].
   bf16x8_t qf[2][KS];
   static_for<2>([&](auto a) {
     const int row = r0 + a * 32 + frow;
     static_for<KS>([&](auto s) {
-      if (row < T) {
-        qf[a][s] = *reinterpret_cast<const bf16x8_t*>(Qb + row * row_stride + s * 16 + fk);
-      } else {
-        qf[a][s] = bf16x8_t{};
-      }
+      if (row < T) qf[a][s] = *reinterpret_cast<const bf16x8_t*>(Qb + row * row_stride + s * 16 + fk);
+      else qf[a][s] = bf16x8_t{};
     });
   });
 
   const int kend = causal ? min(T, (qb + 1) * kQB) : T;
-  const int nkb = (kend + kKB - 1) / kKB;
+  const int nkb = (kend + KB - 1) / KB;
 
-  // key staging map: chunk c covers key (tid / (D/8) + c * 256/(D/8)), column 8*(tid % (D/8))
-  constexpr int CPR = D / 8;  // chunks per key row
+  const int lrow = tid / CPR, lcol = (tid % CPR) * 8;
   u32x4_t rk[NCH];
   auto gload = [&](int kb) {
     static_for<NCH>([&](auto c) {
-      const int kr = tid / CPR + c * (256 / CPR);
-      const int j = kb * kKB + kr;
-      if (j < T)
-        rk[c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + (tid % CPR) * 8);
-      else
-        rk[c] = u32x4_t{};
+      const int j = kb * KB + lrow + c * RPP;
+      if (j < T) rk[c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + lcol);
+      else rk[c] = u32x4_t{};
     });
   };
   auto sstore = [&](int buf) {
     static_for<NCH>([&](auto c) {
-      const int kr = tid / CPR + c * (256 / CPR);
-      *reinterpret_cast<u32x4_t*>(&sK[buf][kr * PITCH + (tid % CPR) * 8]) = rk[c];
+      *reinterpret_cast<u32x4_t*>(&sK[buf][(lrow + c * RPP) * PITCH + lcol]) = rk[c];
     });
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS traffic done
+    __builtin_amdgcn_s_barrier();
   };
 
   float m = -INFINITY;
@@ -95,47 +100,56 @@ __global__ __launch_bounds__(256) void qk_rowmax_kernel(const bf16_t* __restrict
 
   gload(0);
   sstore(0);
-  __syncthreads();
+  barrier();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
     const bool more = kb + 1 < nkb;
     if (more) gload(kb + 1);
-    const int c0 = kb * kKB;
-    // This wave's rows r0 .. r0+63 see keys c0 .. c0+63 unless all are masked.
+    const int c0 = kb * KB;
     const bool any = (r0 < T) && (!causal || c0 <= r0 + 63);
     if (any) {
-      f32x16_t acc[2][2];
-      static_for<4>([&](auto ab) { acc[ab / 2][ab % 2] = f32x16_t{}; });
+      f32x16_t acc[2][NB];
+      static_for<2 * NB>([&](auto ab) { acc[ab / NB][ab % NB] = f32x16_t{}; });
       const bf16_t* sKc = sK[cur];
       static_for<KS>([&](auto s) {
-        bf16x8_t kf[2];
-        static_for<2>([&](auto n) {
+        bf16x8_t kf[NB];
+        static_for<NB>([&](auto n) {
           kf[n] = *reinterpret_cast<const bf16x8_t*>(&sKc[(n * 32 + frow) * PITCH + s * 16 + fk]);
         });
-        static_for<4>([&](auto ab) {
-          constexpr int A = decltype(ab)::value / 2, N = decltype(ab)::value % 2;
+        static_for<2 * NB>([&](auto ab) {
+          constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
           acc[A][N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[A][s], kf[N], acc[A][N], 0, 0, 0);
         });
       });
-      // Unmasked block: every (i, j) valid.
-      const bool full = (!causal || c0 + 63 <= r0) && (r0 + 63 < T) && (c0 + 63 < T);
-      static_for<4>([&](auto ab) {
-        constexpr int A = decltype(ab)::value / 2, N = decltype(ab)::value % 2;
-        const int j = c0 + N * 32 + (lane & 31);
-        static_for<16>([&](auto e) {
-          constexpr int E = decltype(e)::value;
-          const float v = acc[A][N][E];
-          const int i = r0 + A * 32 + 8 * (E / 4) + 4 * (lane >> 5) + (E % 4);
-          const bool ok = full || (i < T && j < T && (!causal || j <= i));
-          if (ok) {
+      const bool full = (!causal || c0 + KB - 1 <= r0) && (r0 + 63 < T) && (c0 + KB - 1 < T);
+      if (full) {
+        static_for<2 * NB>([&](auto ab) {
+          constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
+          static_for<16>([&](auto e) {
+            constexpr int E = decltype(e)::value;
+            const float v = acc[A][N][E];
             m = fmaxf(m, v);
             has_nan |= (v != v);
-          }
+          });
         });
-      });
+      } else {
+        static_for<2 * NB>([&](auto ab) {
+          constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
+          const int j = c0 + N * 32 + (lane & 31);
+          static_for<16>([&](auto e) {
+            constexpr int E = decltype(e)::value;
+            const float v = acc[A][N][E];
+            const int i = r0 + A * 32 + 8 * (E / 4) + 4 * (lane >> 5) + (E % 4);
+            if (i < T && j < T && (!causal || j <= i)) {
+              m = fmaxf(m, v);
+              has_nan |= (v != v);
+            }
+          });
+        });
+      }
     }
     if (more) sstore(cur ^ 1);
-    __syncthreads();
+    barrier();
   }
 
   m = wave_max(m);
@@ -146,8 +160,13 @@ __global__ __launch_bounds__(256) void qk_rowmax_kernel(const bf16_t* __restrict
   }
   __syncthreads();
   if (tid == 0) {
-    float r = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    if (wnan[0] | wnan[1] | wnan[2] | wnan[3]) r = __uint_as_float(0x7fc00000u);
+    float r = wmax[0];
+    int nan = wnan[0];
+    for (int w = 1; w < 8; ++w) {
+      r = fmaxf(r, wmax[w]);
+      nan |= wnan[w];
+    }
+    if (nan) r = __uint_as_float(0x7fc00000u);
     partial[(static_cast<int64_t>(b) * H + h) * nqb + qb] = r;
   }
 }
@@ -230,13 +249,13 @@ hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int 
   const int nblocks = B * H * nqb;
   switch (d_head) {
     case 64:
-      hipLaunchKernelGGL(qk_rowmax_kernel<64>, dim3(nblocks), dim3(256), 0, s, Q, K, B, T, H, causal, partial, nqb);
+      hipLaunchKernelGGL(qk_rowmax_kernel<64>, dim3(nblocks), dim3(kThreads), 0, s, Q, K, B, T, H, causal, partial, nqb);
       break;
     case 128:
-      hipLaunchKernelGGL(qk_rowmax_kernel<128>, dim3(nblocks), dim3(256), 0, s, Q, K, B, T, H, causal, partial, nqb);
+      hipLaunchKernelGGL(qk_rowmax_kernel<128>, dim3(nblocks), dim3(kThreads), 0, s, Q, K, B, T, H, causal, partial, nqb);
       break;
     case 256:
-      hipLaunchKernelGGL(qk_rowmax_kernel<256>, dim3(nblocks), dim3(256), 0, s, Q, K, B, T, H, causal, partial, nqb);
+      hipLaunchKernelGGL(qk_rowmax_kernel<256>, dim3(nblocks), dim3(kThreads), 0, s, Q, K, B, T, H, causal, partial, nqb);
       break;
     default:
       return hipErrorInvalidValue;
