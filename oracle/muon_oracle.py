@@ -283,3 +283,27 @@ def qkclip_rescale_mla(Wqc: np.ndarray, Wkc: np.ndarray, Wqr: np.ndarray,
         Wkc[h * d_c:(h + 1) * d_c] *= math.sqrt(g)
         Wqr[h * d_r:(h + 1) * d_r] *= g
     return Wqc, Wkc, Wqr, Wkr, gamma, flag
+
+
+# ---------------------------------------------------------------------------
+# AdamW, the companion optimizer for the parameters Muon does not take.
+# ---------------------------------------------------------------------------
+
+
+def adamw_step(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, *,
+               lr: float, beta1: float, beta2: float, eps: float,
+               weight_decay: float, step: int):
+    """One decoupled AdamW step, float64 ("MuonClip" section 03 and section 07
+    pseudocode route embeddings, the head and 1-D parameters to AdamW; the
+    pages name it without writing it out, so this is the standard decoupled
+    form): p <- p (1 - lr wd); m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
+    p <- p - lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+    `step` is t >= 1 (the step being taken).  Returns (p, m, v)."""
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    mhat = m / (1.0 - beta1 ** step)
+    vhat = v / (1.0 - beta2 ** step)
+    p = p * (1.0 - lr * weight_decay) - lr * mhat / (np.sqrt(vhat) + eps)
+    return p, m, v
