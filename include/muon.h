@@ -15,8 +15,9 @@
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers unless stated otherwise; the structs
- *     passed by pointer (muon_group_t arrays, muon_hparams_t) are HOST memory
- *     read during the call only.
+ *     passed by pointer (muon_group_t, qkclip_slice_t and adamw_tensor_t
+ *     arrays, muon_hparams_t, adamw_hparams_t) are HOST memory read during
+ *     the call only.
  *   - Matrices are row-major [rows][cols] with rows = fan-out (the layout of
  *     a Linear weight).  A group is `batch` same-shape matrices, matrix b
  *     starting `batch_stride` elements after matrix b-1.
@@ -184,6 +185,69 @@ int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H,
 int qkclip_rescale(void* Wq, void* Wk, int dtype, int H, int d_head,
                    int d_model, const float* s_max, float tau, float alpha,
                    int32_t* clipped, hipStream_t stream);
+
+/* ---------------------------------------------------- qkclip_rescale_slices
+ * The same per-head rule over up to QKCLIP_MAX_SLICES row slices, for any
+ * layout in which each head owns a run of consecutive rows: head h owns rows
+ * [h*head_pitch, h*head_pitch + rows_per_head) counted from `w` (a device
+ * pointer of `dtype`, row-major, `cols` elements per row), and for a clipped
+ * head those rows are multiplied by gamma^exponent, exponent in [0, 1].
+ * head_pitch > rows_per_head describes fused projections whose per-head
+ * blocks interleave several parts (point `w` at the part's first row).
+ * Slices must not overlap.  s_max, tau, clipped as for qkclip_rescale.     */
+#define QKCLIP_MAX_SLICES 4
+typedef struct {
+  void* w;
+  int64_t head_pitch;   /* rows between the first rows of heads h and h+1 */
+  int rows_per_head;
+  int cols;
+  float exponent;
+} qkclip_slice_t;
+int qkclip_rescale_slices(const qkclip_slice_t* slices, int n_slices,
+                          int dtype, int H, const float* s_max, float tau,
+                          int32_t* clipped, hipStream_t stream);
+
+/* -------------------------------------------------------- qkclip_rescale_mla
+ * QK-Clip for multi-head latent attention ([MC] 06; [MM] "MuonClip: QK-clip,
+ * per head, adapted to MLA"): for a clipped head the head-specific content query rows
+ * (Wqc, [H*d_c][q_cols]) and content key rows (Wkc, [H*d_c][kv_cols]) are
+ * multiplied by sqrt(gamma), the head-specific rotary query rows (Wqr,
+ * [H*d_r][q_cols]) by gamma, and the rotary key shared by all heads is left
+ * alone (it takes no argument).  Equivalent to qkclip_rescale_slices with
+ * exponents 1/2, 1/2, 1.                                                    */
+int qkclip_rescale_mla(void* Wqc, void* Wkc, void* Wqr, int dtype, int H,
+                       int d_c, int d_r, int q_cols, int kv_cols,
+                       const float* s_max, float tau, int32_t* clipped,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------- adamw_step
+ * Decoupled AdamW for the parameters outside Muon's 2-D hidden matrices
+ * (embeddings, output head, norms, biases: [MC] 03 routing and 07 step; the
+ * pages name AdamW without writing it out, so this is the standard form):
+ *   m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p (1 - lr wd) - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * with t = hp->step >= 1.  Each tensor is a flat run of `numel` elements:
+ * param and grad of `dtype` (bf16 rounds p once, RNE), exp_avg and
+ * exp_avg_sq fp32, all updated in place except grad.  Any number of tensors
+ * per call; they are packed into as few launches as the argument block
+ * allows.  numel == 0 entries are skipped.  fp32 arithmetic.                */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+  int step;
+} adamw_hparams_t;
+typedef struct {
+  void* param;
+  const void* grad;
+  float* exp_avg;
+  float* exp_avg_sq;
+  int64_t numel;
+} adamw_tensor_t;
+int adamw_step(const adamw_tensor_t* tensors, int n_tensors, int dtype,
+               const adamw_hparams_t* hp, hipStream_t stream);
 
 /* -------------------------------------------------------------- diagnostics */
 const char* muon_status_string(int status);

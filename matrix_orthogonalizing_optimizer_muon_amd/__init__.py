@@ -50,6 +50,23 @@ class _WsLayout(ctypes.Structure):
                 ("x0_ld", ctypes.c_int64)]
 
 
+class _Slice(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("head_pitch", ctypes.c_int64),
+                ("rows_per_head", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("exponent", ctypes.c_float)]
+
+
+class _AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32)]
+
+
+class _AdamWTensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("numel", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -84,6 +101,12 @@ def load_library() -> ctypes.CDLL:
     lib.qkclip_rowmax.restype = i32
     lib.qkclip_rescale.argtypes = [vp, vp, i32, i32, i32, i32, vp, f32, f32, vp, vp]
     lib.qkclip_rescale.restype = i32
+    lib.qkclip_rescale_slices.argtypes = [ctypes.POINTER(_Slice), i32, i32, i32, vp, f32, vp, vp]
+    lib.qkclip_rescale_slices.restype = i32
+    lib.qkclip_rescale_mla.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, vp, vp]
+    lib.qkclip_rescale_mla.restype = i32
+    lib.adamw_step.argtypes = [ctypes.POINTER(_AdamWTensor), i32, i32, ctypes.POINTER(_AdamWHParams), vp]
+    lib.adamw_step.restype = i32
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_profile_enable.argtypes = [i32]
@@ -313,6 +336,106 @@ def qkclip_rescale(Wq, Wk, s_max, d_head: int, tau: float = 100.0, alpha: float 
                               s_max.data_ptr(), tau, alpha, clipped.data_ptr(), _stream()),
            "qkclip_rescale")
     return clipped
+
+
+def _flags(H, device, clipped):
+    torch = _torch()
+    if clipped is None:
+        clipped = torch.empty(H, dtype=torch.int32, device=device)
+    elif clipped.dtype != torch.int32 or clipped.numel() != H:
+        raise ValueError("clipped must be int32 [H]")
+    return clipped
+
+
+def qkclip_rescale_slices(slices, s_max, tau: float = 100.0, clipped=None):
+    """Per-head rescale over row slices.  Each slice is a tuple
+    (W, row_offset, head_pitch, rows_per_head, exponent) with W a contiguous
+    2-D tensor; head h owns rows row_offset + h*head_pitch + [0, rows_per_head)
+    of W, multiplied by gamma^exponent when the head is clipped.  Returns the
+    int32 [H] flags."""
+    torch = _torch()
+    lib = load_library()
+    H = s_max.numel()
+    if s_max.dtype != torch.float32 or H < 1:
+        raise ValueError("s_max must be float32 [H]")
+    _need_cuda(s_max)
+    arr = (_Slice * max(len(slices), 1))()
+    dtype = None
+    for i, (W, off, pitch, rows, expo) in enumerate(slices):
+        _need_cuda(W)
+        if W.dim() != 2 or not W.is_contiguous():
+            raise ValueError("slice matrices must be contiguous 2-D tensors")
+        code = _dtype_code(W)
+        if dtype is not None and code != dtype:
+            raise TypeError("all slices must share a dtype")
+        dtype = code
+        if off < 0 or rows < 1 or pitch < rows or off + (H - 1) * pitch + rows > W.shape[0]:
+            raise ValueError(f"slice {i}: rows of head {H - 1} fall outside the matrix")
+        arr[i] = _Slice(W.data_ptr() + off * W.shape[1] * W.element_size(), pitch, rows, W.shape[1],
+                        float(expo))
+    clipped = _flags(H, s_max.device, clipped)
+    _check(lib.qkclip_rescale_slices(arr, len(slices), dtype if dtype is not None else DTYPE_BF16, H,
+                                     s_max.data_ptr(), tau, clipped.data_ptr(), _stream()),
+           "qkclip_rescale_slices")
+    return clipped
+
+
+def qkclip_rescale_mla(Wqc, Wkc, Wqr, s_max, d_c: int, d_r: int, tau: float = 100.0, clipped=None):
+    """MLA QK-Clip in place: content query/key rows of a clipped head scale by
+    sqrt(gamma), its rotary query rows by gamma; the shared rotary key is not
+    an argument because it never changes.  Wqc [H*d_c, q_in], Wkc
+    [H*d_c, kv_in], Wqr [H*d_r, q_in].  Returns the int32 [H] flags."""
+    torch = _torch()
+    lib = load_library()
+    _need_cuda(Wqc, Wkc, Wqr, s_max)
+    for W in (Wqc, Wkc, Wqr):
+        if W.dim() != 2 or not W.is_contiguous():
+            raise ValueError("MLA matrices must be contiguous 2-D tensors")
+    if not (Wqc.dtype == Wkc.dtype == Wqr.dtype):
+        raise TypeError("MLA matrices must share a dtype")
+    H = s_max.numel()
+    if s_max.dtype != torch.float32:
+        raise ValueError("s_max must be float32 [H]")
+    if Wqc.shape[0] != H * d_c or Wkc.shape[0] != H * d_c or Wqr.shape[0] != H * d_r:
+        raise ValueError("row counts must be H*d_c (content) and H*d_r (rotary query)")
+    if Wqr.shape[1] != Wqc.shape[1]:
+        raise ValueError("content and rotary query projections must share their input width")
+    clipped = _flags(H, s_max.device, clipped)
+    _check(lib.qkclip_rescale_mla(Wqc.data_ptr(), Wkc.data_ptr(), Wqr.data_ptr(), _dtype_code(Wqc), H, d_c, d_r,
+                                  Wqc.shape[1], Wkc.shape[1], s_max.data_ptr(), tau, clipped.data_ptr(),
+                                  _stream()),
+           "qkclip_rescale_mla")
+    return clipped
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, beta1: float = 0.9,
+               beta2: float = 0.95, eps: float = 1e-8, weight_decay: float = 0.1, step: int = 1):
+    """One AdamW step in place over lists of tensors (params and grads of one
+    dtype, fp32 or bf16; moments fp32; every tensor contiguous)."""
+    torch = _torch()
+    lib = load_library()
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs must have one entry per tensor")
+    arr = (_AdamWTensor * max(n, 1))()
+    dtype = None
+    for i, (p, g, m, v) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
+        _need_cuda(p, g, m, v)
+        code = _dtype_code(p)
+        if dtype is not None and code != dtype:
+            raise TypeError("all params must share a dtype")
+        dtype = code
+        if g.dtype != p.dtype or m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise TypeError("grad must match the param dtype; moments must be float32")
+        if not (p.numel() == g.numel() == m.numel() == v.numel()):
+            raise ValueError(f"tensor {i}: sizes differ")
+        for t in (p, g, m, v):
+            if not t.is_contiguous():
+                raise ValueError("AdamW tensors must be contiguous")
+        arr[i] = _AdamWTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), p.numel())
+    hp = _AdamWHParams(lr, beta1, beta2, eps, weight_decay, step)
+    _check(lib.adamw_step(arr, n, dtype if dtype is not None else DTYPE_F32, ctypes.byref(hp), _stream()),
+           "adamw_step")
 
 
 def profile_enable(on: bool = True):

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "common.hpp"
@@ -256,11 +257,14 @@ GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b,
     q.mvalid = p.mp; q.nvalid = p.mp;
   } else {
     const int TN = p.np / p.tile;
-    q.P = B; q.Q = Xt; q.sP = sa; q.sQ = sx; q.ldp = p.mp; q.ldq = p.mp; q.K = p.mp;
+    // c == 0 (a cubic polynomial): B = bA, so the product takes A and folds b
+    // into the accumulator scale instead of forming B.
+    const bool cubic = (c == 0.0f);
+    q.P = cubic ? A : B; q.Q = Xt; q.sP = sa; q.sQ = sx; q.ldp = p.mp; q.ldq = p.mp; q.K = p.mp;
     q.Et = Xt; q.sEt = sx; q.lde = p.mp;
     q.tm = T; q.tn = TN; q.sym = 0; q.tiles_per_mat = T * TN;
     q.alpha_pow = (t == 0) ? 1 : 0;
-    q.c_acc = 1.0f; q.c_e = a;
+    q.c_acc = cubic ? b : 1.0f; q.c_e = a;
     const bool last = (t == steps - 1);
     if (!last) {
       q.C = Xn; q.sC = sx; q.ldc = p.np;
@@ -288,6 +292,7 @@ int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c,
   static const int kinds[3] = {KIND_NS_SYRK, KIND_NS_POLY, KIND_NS_BX};
   for (int t = 0; t < steps; ++t) {
     for (int stage = 0; stage < 3; ++stage) {
+      if (stage == STAGE_POLY && c == 0.0f) continue;
       for (int tile : {256, 128}) {
         GemmLaunch L{};
         int tiles = 0;
@@ -464,14 +469,96 @@ int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int
   return MUON_OK;
 }
 
+int qkclip_rescale_slices(const qkclip_slice_t* slices, int n_slices, int dtype, int H, const float* s_max,
+                          float tau, int32_t* clipped, hipStream_t stream) {
+  if (!slices || n_slices < 1 || n_slices > QKCLIP_MAX_SLICES || !s_max || H < 1 || H > 65535)
+    return MUON_ERR_INVALID_ARG;
+  if (dtype != MUON_DTYPE_F32 && dtype != MUON_DTYPE_BF16) return MUON_ERR_INVALID_ARG;
+  if (!(tau > 0.0f) || !isfinite(tau)) return MUON_ERR_INVALID_ARG;
+  RescaleLaunch L{};
+  L.nmat = n_slices;
+  for (int z = 0; z < n_slices; ++z) {
+    const qkclip_slice_t& q = slices[z];
+    if (!q.w || q.rows_per_head < 1 || q.cols < 1 || q.head_pitch < q.rows_per_head) return MUON_ERR_INVALID_ARG;
+    if (!(q.exponent >= 0.0f && q.exponent <= 1.0f)) return MUON_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(q.rows_per_head) * q.cols > (int64_t(1) << 40)) return MUON_ERR_INVALID_ARG;
+    if (q.head_pitch > (int64_t(1) << 40) / q.cols) return MUON_ERR_INVALID_ARG;
+    RescaleMat& R = L.m[z];
+    R.W = q.w;
+    R.head_pitch = q.head_pitch;
+    R.rows_per_head = q.rows_per_head;
+    R.cols = q.cols;
+    R.expo = q.exponent;
+    R.vec = (q.cols % 8 == 0) && aligned(q.w, 16);
+  }
+  MUON_LAUNCH(KIND_QK_RESCALE, stream, launch_qk_rescale(L, dtype, H, s_max, tau, clipped, stream));
+  return MUON_OK;
+}
+
 int qkclip_rescale(void* Wq, void* Wk, int dtype, int H, int d_head, int d_model, const float* s_max, float tau,
                    float alpha, int32_t* clipped, hipStream_t stream) {
-  if (!Wq || !Wk || !s_max || H < 1 || d_head < 1 || d_model < 1) return MUON_ERR_INVALID_ARG;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return MUON_ERR_INVALID_ARG;
+  if (d_head < 1) return MUON_ERR_INVALID_ARG;
+  const qkclip_slice_t sl[2] = {{Wq, d_head, d_head, d_model, alpha}, {Wk, d_head, d_head, d_model, 1.0f - alpha}};
+  return qkclip_rescale_slices(sl, 2, dtype, H, s_max, tau, clipped, stream);
+}
+
+int qkclip_rescale_mla(void* Wqc, void* Wkc, void* Wqr, int dtype, int H, int d_c, int d_r, int q_cols,
+                       int kv_cols, const float* s_max, float tau, int32_t* clipped, hipStream_t stream) {
+  if (d_c < 1 || d_r < 1) return MUON_ERR_INVALID_ARG;
+  const qkclip_slice_t sl[3] = {{Wqc, d_c, d_c, q_cols, 0.5f}, {Wkc, d_c, d_c, kv_cols, 0.5f},
+                                {Wqr, d_r, d_r, q_cols, 1.0f}};
+  return qkclip_rescale_slices(sl, 3, dtype, H, s_max, tau, clipped, stream);
+}
+
+int adamw_step(const adamw_tensor_t* tensors, int n_tensors, int dtype, const adamw_hparams_t* hp,
+               hipStream_t stream) {
+  if (!tensors || n_tensors < 0 || !hp) return MUON_ERR_INVALID_ARG;
   if (dtype != MUON_DTYPE_F32 && dtype != MUON_DTYPE_BF16) return MUON_ERR_INVALID_ARG;
-  if (!(tau > 0.0f) || !isfinite(tau) || !(alpha >= 0.0f && alpha <= 1.0f)) return MUON_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(d_head) * d_model > (int64_t(1) << 31) / 2) return MUON_ERR_INVALID_ARG;
-  MUON_LAUNCH(KIND_QK_RESCALE, stream,
-              launch_qk_rescale(Wq, Wk, dtype, H, d_head, d_model, s_max, tau, alpha, clipped, stream));
+  if (hp->step < 1 || !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) ||
+      !(hp->eps > 0.0f) || !isfinite(hp->lr) || !isfinite(hp->weight_decay))
+    return MUON_ERR_INVALID_ARG;
+  const size_t esz = dtype == MUON_DTYPE_BF16 ? 2 : 4;
+  for (int i = 0; i < n_tensors; ++i) {
+    const adamw_tensor_t& t = tensors[i];
+    if (t.numel < 0 || t.numel > (int64_t(1) << 40)) return MUON_ERR_INVALID_ARG;
+    if (t.numel > 0 && (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq)) return MUON_ERR_INVALID_ARG;
+    if (t.numel > 0 && (!aligned(t.param, esz) || !aligned(t.grad, esz) || !aligned(t.exp_avg, 4) ||
+                        !aligned(t.exp_avg_sq, 4)))
+      return MUON_ERR_INVALID_ARG;
+  }
+  AdamWLaunch A{};
+  A.lr = hp->lr;
+  A.beta1 = hp->beta1;
+  A.beta2 = hp->beta2;
+  A.eps = hp->eps;
+  A.decay = static_cast<float>(1.0 - static_cast<double>(hp->lr) * hp->weight_decay);
+  A.c1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta1), hp->step)));
+  A.c2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta2), hp->step)));
+  int i = 0;
+  while (i < n_tensors) {
+    A.ntensors = 0;
+    int64_t blocks = 0;
+    for (; i < n_tensors && A.ntensors < kAdamWMaxTensors; ++i) {
+      const adamw_tensor_t& t = tensors[i];
+      if (t.numel == 0) continue;
+      const int64_t nb = (t.numel + 2047) / 2048;
+      if (A.ntensors > 0 && blocks + nb > (int64_t(1) << 30)) break;
+      AdamWTensor& T = A.t[A.ntensors];
+      T.p = t.param;
+      T.g = t.grad;
+      T.m = t.exp_avg;
+      T.v = t.exp_avg_sq;
+      T.n = t.numel;
+      T.vec = aligned(t.param, 16) && aligned(t.grad, 16) && aligned(t.exp_avg, 16) && aligned(t.exp_avg_sq, 16);
+      A.blk_start[A.ntensors] = static_cast<int>(blocks);
+      blocks += nb;
+      ++A.ntensors;
+    }
+    if (A.ntensors == 0) break;
+    A.blk_start[A.ntensors] = static_cast<int>(blocks);
+    MUON_LAUNCH(KIND_ADAMW, stream, launch_adamw(A, dtype, static_cast<int>(blocks), stream));
+  }
   return MUON_OK;
 }
 
@@ -505,7 +592,7 @@ int muon_profile_collect(double* total_ms, int64_t* launches, int n_kinds) {
 const char* muon_kernel_kind_name(int kind) {
   static const char* names[KIND_COUNT] = {"momentum_norm", "norm_finalize", "ns_syrk_xxt", "ns_syrk_poly",
                                           "ns_gemm_bx",    "param_update",  "qk_rowmax",   "qk_reduce",
-                                          "qk_rescale"};
+                                          "qk_rescale",    "adamw"};
   if (kind < 0 || kind >= KIND_COUNT) return "unknown";
   return names[kind];
 }

@@ -66,7 +66,8 @@ enum KernelKind {
   KIND_QK_ROWMAX = 6,
   KIND_QK_REDUCE = 7,
   KIND_QK_RESCALE = 8,
-  KIND_COUNT = 9
+  KIND_ADAMW = 9,
+  KIND_COUNT = 10
 };
 
 // ---------------------------------------------------------------------------
@@ -166,9 +167,44 @@ hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int 
                             int causal, float* partial, int nqb, hipStream_t s);
 hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float logit_scale,
                             float* s_max, hipStream_t s);
-hipError_t launch_qk_rescale(void* Wq, void* Wk, int dtype, int H, int d_head, int d_model,
-                             const float* s_max, float tau, float alpha, int32_t* clipped,
-                             hipStream_t s);
+// Per-head row rescale of up to kMaxRescaleSlices row slices: head h owns
+// rows [h * head_pitch, h * head_pitch + rows_per_head) of m[z].W (cols
+// elements per row), scaled by gamma^expo.
+constexpr int kMaxRescaleSlices = 4;
+struct RescaleMat {
+  void* W;
+  int64_t head_pitch;  // rows
+  int rows_per_head;
+  int cols;
+  float expo;
+  int vec;             // 16-byte aligned, cols a multiple of 8
+};
+struct RescaleLaunch {
+  int nmat;
+  RescaleMat m[kMaxRescaleSlices];
+};
+hipError_t launch_qk_rescale(const RescaleLaunch& L, int dtype, int H, const float* s_max, float tau,
+                             int32_t* clipped, hipStream_t s);
+
+// Multi-tensor AdamW: block b of a launch works on tensor t with
+// blk_start[t] <= b < blk_start[t + 1], elements (b - blk_start[t]) * 2048 ...
+constexpr int kAdamWMaxTensors = 48;
+struct AdamWTensor {
+  void* p;
+  const void* g;
+  float* m;
+  float* v;
+  int64_t n;
+  int vec;  // p, g, m, v all 16-byte aligned
+};
+struct AdamWLaunch {
+  int ntensors;
+  float lr, beta1, beta2, eps, decay;  // decay = 1 - lr * weight_decay
+  float c1, c2;                        // 1 / (1 - beta^t) bias corrections
+  int blk_start[kAdamWMaxTensors + 1];
+  AdamWTensor t[kAdamWMaxTensors];
+};
+hipError_t launch_adamw(const AdamWLaunch& A, int dtype, int blocks, hipStream_t s);
 
 // Profiler hooks (api.hip).
 void prof_begin(int kind, hipStream_t s);

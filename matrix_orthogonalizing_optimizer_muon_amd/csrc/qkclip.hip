@@ -14,6 +14,8 @@
 // staged through LDS, the logits never stored.  Maxima are reduced across the wavefront with
 // cross-lane max, across the block through LDS, and across blocks by a
 // second, fixed-order kernel (no atomics, no initialisation pass).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace muon {
@@ -191,31 +193,31 @@ __global__ __launch_bounds__(64) void qk_reduce_kernel(const float* __restrict__
   if (threadIdx.x == 0) s_max[h] = nan ? __uint_as_float(0x7fc00000u) : m * logit_scale;
 }
 
-// Rescale the rows of one head in W_q (z = 0) or W_k (z = 1).
+// Rescale the rows of head h (blockIdx.y) in slice z (blockIdx.z) by
+// gamma^expo, gamma = tau / S_max^h, when S_max^h is finite and > tau.
+// The common exponents take exact paths (sqrt for 1/2, gamma itself for 1).
 template <typename WT>
-__global__ __launch_bounds__(256) void qk_rescale_kernel(WT* __restrict__ Wq, WT* __restrict__ Wk,
-                                                         int d_head, int d_model,
-                                                         const float* __restrict__ s_max, float tau,
-                                                         float alpha, int32_t* __restrict__ clipped,
-                                                         int vec) {
+__global__ __launch_bounds__(256) void qk_rescale_kernel(RescaleLaunch L, const float* __restrict__ s_max,
+                                                         float tau, int32_t* __restrict__ clipped) {
   const int h = blockIdx.y, z = blockIdx.z;
   const float s = s_max[h];
   const bool finite = (__float_as_uint(s) & 0x7f800000u) != 0x7f800000u;
   const bool clip = finite && (s > tau);
   if (clipped && blockIdx.x == 0 && z == 0 && threadIdx.x == 0) clipped[h] = finite ? (clip ? 1 : 0) : -1;
   if (!clip) return;
+  const RescaleMat& R = L.m[z];
+  const int64_t n = static_cast<int64_t>(R.rows_per_head) * R.cols;
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (e0 >= n) return;
   const float gamma = tau / s;
-  const float ex = (z == 0) ? alpha : 1.0f - alpha;
+  const float ex = R.expo;
   float f;
   if (ex == 0.5f) f = sqrtf(gamma);
   else if (ex == 1.0f) f = gamma;
   else if (ex == 0.0f) f = 1.0f;
   else f = powf(gamma, ex);
-  WT* W = (z == 0 ? Wq : Wk) + static_cast<int64_t>(h) * d_head * d_model;
-  const int64_t n = static_cast<int64_t>(d_head) * d_model;
-  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
-  if (e0 >= n) return;
-  if (vec && e0 + 7 < n) {
+  WT* W = static_cast<WT*>(R.W) + static_cast<int64_t>(h) * R.head_pitch * R.cols;
+  if (R.vec && e0 + 7 < n) {
     if constexpr (sizeof(WT) == 2) {
       u32x4_t w = *reinterpret_cast<const u32x4_t*>(W + e0);
       static_for<4>([&](auto q) {
@@ -269,23 +271,15 @@ hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float l
   return hipGetLastError();
 }
 
-hipError_t launch_qk_rescale(void* Wq, void* Wk, int dtype, int H, int d_head, int d_model,
-                             const float* s_max, float tau, float alpha, int32_t* clipped,
-                             hipStream_t s) {
-  const int64_t n = static_cast<int64_t>(d_head) * d_model;
-  const int bx = static_cast<int>((n + 2047) / 2048);
-  const int vec = (d_model % 8 == 0) &&
-                  (reinterpret_cast<uintptr_t>(Wq) % 16 == 0) && (reinterpret_cast<uintptr_t>(Wk) % 16 == 0) &&
-                  (dtype == MUON_DTYPE_BF16 ? true : (d_model % 8 == 0));
-  const int vec_ok = dtype == MUON_DTYPE_BF16 ? vec : (vec && (reinterpret_cast<uintptr_t>(Wq) % 32 == 0));
+hipError_t launch_qk_rescale(const RescaleLaunch& L, int dtype, int H, const float* s_max, float tau,
+                             int32_t* clipped, hipStream_t s) {
+  int64_t nmax = 0;
+  for (int z = 0; z < L.nmat; ++z) nmax = std::max<int64_t>(nmax, static_cast<int64_t>(L.m[z].rows_per_head) * L.m[z].cols);
+  const int bx = static_cast<int>((nmax + 2047) / 2048);
   if (dtype == MUON_DTYPE_BF16)
-    hipLaunchKernelGGL(qk_rescale_kernel<bf16_t>, dim3(bx, H, 2), dim3(256), 0, s,
-                       static_cast<bf16_t*>(Wq), static_cast<bf16_t*>(Wk), d_head, d_model, s_max, tau,
-                       alpha, clipped, vec_ok);
+    hipLaunchKernelGGL(qk_rescale_kernel<bf16_t>, dim3(bx, H, L.nmat), dim3(256), 0, s, L, s_max, tau, clipped);
   else
-    hipLaunchKernelGGL(qk_rescale_kernel<float>, dim3(bx, H, 2), dim3(256), 0, s,
-                       static_cast<float*>(Wq), static_cast<float*>(Wk), d_head, d_model, s_max, tau,
-                       alpha, clipped, vec_ok);
+    hipLaunchKernelGGL(qk_rescale_kernel<float>, dim3(bx, H, L.nmat), dim3(256), 0, s, L, s_max, tau, clipped);
   return hipGetLastError();
 }
 

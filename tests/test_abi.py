@@ -26,9 +26,10 @@ def lib():
     return mm.load_library()
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["muon_step", "ns_orthogonalize", "qkclip_rowmax", "qkclip_rescale"]:
+    for n in ["muon_step", "ns_orthogonalize", "qkclip_rowmax", "qkclip_rescale",
+              "qkclip_rescale_slices", "qkclip_rescale_mla", "adamw_step"]:
         assert n in names
 
 
@@ -71,6 +72,32 @@ def test_host_validation_without_gpu(lib):
     assert lib.qkclip_rescale(16, 16, 1, 2, 64, 8, 16, -1.0, 0.5, None, None) == mm.MUON_ERR_INVALID_ARG
     assert lib.qkclip_rescale(16, 16, 1, 2, 64, 8, 16, 100.0, 1.5, None, None) == mm.MUON_ERR_INVALID_ARG
     assert lib.ns_orthogonalize(16, 0, 16, 1, 4, 4, 16, 5, 3.4, -4.7, 2.0, 1e-7, None, 0, None) == mm.MUON_ERR_WORKSPACE
+    # MLA: zero rotary width, bad dtype
+    assert lib.qkclip_rescale_mla(16, 16, 16, 1, 2, 64, 0, 8, 8, 16, 100.0, None, None) == mm.MUON_ERR_INVALID_ARG
+    assert lib.qkclip_rescale_mla(16, 16, 16, 5, 2, 64, 32, 8, 8, 16, 100.0, None, None) == mm.MUON_ERR_INVALID_ARG
+    # slices: too many, pitch below rows, exponent outside [0, 1]
+    sl = (mm._Slice * 5)()
+    for i in range(5):
+        sl[i] = mm._Slice(16, 64, 64, 8, 0.5)
+    assert lib.qkclip_rescale_slices(sl, 5, 1, 2, 16, 100.0, None, None) == mm.MUON_ERR_INVALID_ARG
+    sl[0] = mm._Slice(16, 32, 64, 8, 0.5)
+    assert lib.qkclip_rescale_slices(sl, 1, 1, 2, 16, 100.0, None, None) == mm.MUON_ERR_INVALID_ARG
+    sl[0] = mm._Slice(16, 64, 64, 8, 1.5)
+    assert lib.qkclip_rescale_slices(sl, 1, 1, 2, 16, 100.0, None, None) == mm.MUON_ERR_INVALID_ARG
+    # AdamW: step 0, beta1 = 1, missing moment buffer, misaligned bf16 param
+    t = (mm._AdamWTensor * 1)()
+    t[0] = mm._AdamWTensor(16, 16, 16, 16, 10)
+    hp = mm._AdamWHParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 0)
+    assert lib.adamw_step(t, 1, 1, ctypes.byref(hp), None) == mm.MUON_ERR_INVALID_ARG
+    hp = mm._AdamWHParams(1e-3, 1.0, 0.95, 1e-8, 0.1, 1)
+    assert lib.adamw_step(t, 1, 1, ctypes.byref(hp), None) == mm.MUON_ERR_INVALID_ARG
+    hp = mm._AdamWHParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+    t[0] = mm._AdamWTensor(16, 16, None, 16, 10)
+    assert lib.adamw_step(t, 1, 1, ctypes.byref(hp), None) == mm.MUON_ERR_INVALID_ARG
+    t[0] = mm._AdamWTensor(17, 16, 16, 16, 10)
+    assert lib.adamw_step(t, 1, 1, ctypes.byref(hp), None) == mm.MUON_ERR_INVALID_ARG
+    # nothing to do is not an error and launches nothing
+    assert lib.adamw_step(t, 0, 1, ctypes.byref(hp), None) == mm.MUON_OK
     assert lib.ns_workspace_size(1, 0, 4) == 0
 
 
