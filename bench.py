@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=5000)
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="time torch.matmul (hipBLASLt) on the full, unsymmetric Newton-Schulz "
+                         "products of the same shapes, for comparison, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM counters)")
     return ap.parse_args()
@@ -95,6 +98,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 3}))
+        return
+
+    if args.blas_reference:
+        print(json.dumps(blas_reference(torch)), flush=True)
         return
 
     import matrix_orthogonalizing_optimizer_muon_amd as mm
@@ -218,9 +225,86 @@ def main():
         "heads_clipped_per_step": n_clipped,
     }
 
+    out["companion"] = companion(mm, torch, dev, seed, n_mats * m * n)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
     print(json.dumps(out), flush=True)
+
+
+def blas_reference(torch, reps=10):
+    """hipBLASLt (torch.matmul) on the three products of one Newton-Schulz
+    iteration at the layer's shape (4 matrices, wide 7168 x 8192), computed
+    in full (no symmetry) and without the a X / b A terms.  Operands are
+    contiguous; the result is a reference point, not part of the method."""
+    dev = torch.device("cuda:0")
+    m, n, nb = 7168, 8192, 4
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    Bm = (torch.randn((nb, m, m), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    X = (torch.randn((nb, m, n), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    Xt = X.transpose(1, 2).contiguous()
+    res = {"shapes": "4 x (7168x7168 @ 7168x8192, 7168x8192 @ 8192x7168, 7168x7168 @ 7168x7168)"}
+    for name, f, flop in (("B_X", lambda: torch.matmul(Bm, X), 2.0 * nb * m * m * n),
+                          ("X_Xt_full", lambda: torch.matmul(X, Xt), 2.0 * nb * m * m * n),
+                          ("A_A_full", lambda: torch.matmul(Bm, Bm), 2.0 * nb * m * m * m)):
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 1)}
+    res["ns_iteration_ms"] = round(sum(v["ms"] for k, v in res.items() if isinstance(v, dict)), 3)
+    return res
+
+
+def companion(mm, torch, dev, seed, n_elem, reps=5):
+    """The parts of a full MuonClip step that sit beside the timed Muon path,
+    timed on their own after it: AdamW over as many parameters as the layer's
+    four matrices hold (bf16 params and grads, fp32 moments: 22 bytes per
+    element) plus two norm weights, and the MLA QK-Clip rescale at a
+    latent-attention shape (64 heads, content 128 and rotary 64 rows per head,
+    query latent 1536, key/value latent 512, every head clipped)."""
+    from synthetic import generators as gen
+    hd, H, d_c, d_r, q_in, kv_in = 7168, 64, 128, 64, 1536, 512
+    P = [gen.bulk_normal_torch((n_elem,), 0.02, seed + 20, dev, torch.bfloat16),
+         torch.ones(hd, dtype=torch.bfloat16, device=dev), torch.ones(hd, dtype=torch.bfloat16, device=dev)]
+    G = [gen.bulk_normal_torch((t.numel(),), 1e-3, seed + 21 + i, dev, torch.bfloat16) for i, t in enumerate(P)]
+    M = [torch.zeros(t.numel(), dtype=torch.float32, device=dev) for t in P]
+    V = [torch.zeros(t.numel(), dtype=torch.float32, device=dev) for t in P]
+    Wqc = gen.bulk_normal_torch((H * d_c, q_in), 0.02, seed + 30, dev, torch.bfloat16)
+    Wkc = gen.bulk_normal_torch((H * d_c, kv_in), 0.02, seed + 31, dev, torch.bfloat16)
+    Wqr = gen.bulk_normal_torch((H * d_r, q_in), 0.02, seed + 32, dev, torch.bfloat16)
+    s_hi = torch.full((H,), 1.0e4, dtype=torch.float32, device=dev)
+    mm.adamw_step(P, G, M, V, lr=3e-4, step=1)
+    mm.qkclip_rescale_mla(Wqc, Wkc, Wqr, s_hi, d_c, d_r)
+    torch.cuda.synchronize()
+    mm.profile_enable(True)
+    for t in range(reps):
+        mm.adamw_step(P, G, M, V, lr=3e-4, step=t + 2)
+        mm.qkclip_rescale_mla(Wqc, Wkc, Wqr, s_hi, d_c, d_r)
+    prof = mm.profile_collect()
+    mm.profile_enable(False)
+    res = {}
+    n_all = sum(t.numel() for t in P)
+    ms, cnt = prof["adamw"]
+    if cnt:
+        by = 22 * n_all
+        t = ms / cnt * 1e-3
+        res["adamw"] = {"params": n_all, "avg_us": round(1e6 * t, 1), "bytes": by,
+                        "GBs": round(by / t / 1e9, 1), "frac_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    ms, cnt = prof["qk_rescale"]
+    if cnt:
+        by = 2 * 2 * H * (d_c * q_in + d_c * kv_in + d_r * q_in)   # bf16 read + write
+        t = ms / cnt * 1e-3
+        res["qkclip_rescale_mla"] = {"avg_us": round(1e6 * t, 2), "bytes": by,
+                                     "GBs": round(by / t / 1e9, 1)}
+    del P, G, M, V, Wqc, Wkc, Wqr
+    return res
 
 
 def cpu_baseline(wl, m, n, n_mats, B, T, H, D):

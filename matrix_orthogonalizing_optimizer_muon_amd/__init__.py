@@ -20,7 +20,7 @@ MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_ER
 DTYPE_F32, DTYPE_BF16 = 0, 1
 SCALE_MODES = {"moonlight": 0, "spectral": 1, "none": 2}
 MAX_GROUPS = 16
-KERNEL_KINDS = 9
+_MAX_KINDS = 64   # upper bound on the library's kernel kinds (it reports the real count)
 
 # ---------------------------------------------------------------------------
 # C structs
@@ -445,9 +445,10 @@ def profile_enable(on: bool = True):
 def profile_collect() -> dict:
     """{kernel kind name: (total_ms, launches)} for launches since profile_enable."""
     lib = load_library()
-    ms = (ctypes.c_double * KERNEL_KINDS)()
-    cnt = (ctypes.c_int64 * KERNEL_KINDS)()
-    n = lib.muon_profile_collect(ms, cnt, KERNEL_KINDS)
+    ms = (ctypes.c_double * _MAX_KINDS)()
+    cnt = (ctypes.c_int64 * _MAX_KINDS)()
+    n = lib.muon_profile_collect(ms, cnt, _MAX_KINDS)
     if n < 0:
         raise MuonError(-n, "muon_profile_collect")
-    return {lib.muon_kernel_kind_name(k).decode(): (ms[k], int(cnt[k])) for k in range(KERNEL_KINDS)}
+    n = min(n, _MAX_KINDS)
+    return {lib.muon_kernel_kind_name(k).decode(): (ms[k], int(cnt[k])) for k in range(n)}
