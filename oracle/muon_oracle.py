@@ -23,7 +23,7 @@ Sources (web pages, cited by title and section):
   [MS]  "About Muon: Muon At Scale" (kiungsong.github.io), sections
         "Why Not Bernstein's Multiplier?", "When Softmax Collapses".
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * Nesterov lookahead: U = G + mu * M_new (sum-form momentum, [MC] 02 says a
     lookahead "may be applied" without giving its form).
   * Normalisation epsilon: X0 = X / (||X||_F + eps), eps = 1e-7 ([MM] writes
@@ -283,6 +283,41 @@ def qkclip_rescale_mla(Wqc: np.ndarray, Wkc: np.ndarray, Wqr: np.ndarray,
         Wkc[h * d_c:(h + 1) * d_c] *= math.sqrt(g)
         Wqr[h * d_r:(h + 1) * d_r] *= g
     return Wqc, Wkc, Wqr, Wkr, gamma, flag
+
+
+# ---------------------------------------------------------------------------
+# The attention forward that the per-head statistic comes from.
+# ---------------------------------------------------------------------------
+
+
+def attention_forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                      logit_scale: float, causal: bool = True):
+    """Softmax attention per batch row b and head h, float64: logits
+    s_ij = logit_scale * q_i . k_j (j <= i when causal), output
+    o_i = sum_j softmax_j(s_ij) v_j, log-sum-exp lse_i = log sum_j exp(s_ij),
+    and the per-head maximum logit of smax_per_head.  The pages take S_max
+    from this forward ([MC] 05: the per-head signal is read off the forward's
+    logits; [MM] "The exploding-logit problem": the logits that feed the
+    softmax), so it is the same maximum.
+
+    Q, K, V: [B, T, H, d].  Returns (O [B, T, H, d], lse [B, H, T], s_max [H])."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, T, H, d = Q.shape
+    O = np.zeros((B, T, H, V.shape[3]))
+    lse = np.zeros((B, H, T))
+    mask = np.tril(np.ones((T, T), dtype=bool)) if causal else np.ones((T, T), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            S = (Q[b, :, h, :] @ K[b, :, h, :].T) * logit_scale
+            S = np.where(mask, S, -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            P = np.exp(S - m)
+            l = P.sum(axis=1, keepdims=True)
+            O[b, :, h, :] = (P @ V[b, :, h, :]) / l
+            lse[b, h, :] = (m + np.log(l))[:, 0]
+    return O, lse, smax_per_head(Q, K, logit_scale, causal)
 
 
 # ---------------------------------------------------------------------------
