@@ -172,6 +172,25 @@ int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H,
                   int d_head, float logit_scale, int causal, float* s_max,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ attn_fwd
+ * Softmax attention forward that also produces QK-Clip's statistic, the way
+ * the pages place it ([MC] 05: the per-head signal is read off the forward;
+ * [MM] "The exploding-logit problem": the logits that feed the softmax):
+ *   s_ij = logit_scale * q_i . k_j  (j <= i if causal, per batch row and head)
+ *   O[b,i,h,:] = sum_j softmax_j(s_ij) V[b,j,h,:]
+ *   lse[b,h,i] = log sum_j exp(s_ij)               (natural log; optional)
+ *   s_max[h]   = max over b, i, j of s_ij           (as qkclip_rowmax)
+ * Q, K, V, O: bf16 [B][T][H][d_head], d_head must be 128; lse: fp32
+ * [B][H][T] or NULL; s_max: fp32 [H].  Scores and the softmax run in fp32,
+ * the probabilities enter the P.V product as bf16, O is rounded once.
+ * A NaN logit makes s_max[h] NaN (and propagates into O).
+ * workspace: >= attn_fwd_workspace_size(B, T, H) bytes, 16-byte aligned.   */
+size_t attn_fwd_workspace_size(int B, int T, int H);
+int attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B,
+             int T, int H, int d_head, float logit_scale, int causal,
+             uint16_t* O, float* lse, float* s_max, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ qkclip_rescale
  * Balanced MHA QK-Clip ([MC] 05 balanced rescale; [MS] "When Softmax
  * Collapses"): for each head h with finite s_max[h] > tau,

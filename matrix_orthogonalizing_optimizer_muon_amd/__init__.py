@@ -105,6 +105,10 @@ def load_library() -> ctypes.CDLL:
     lib.qkclip_rescale_slices.restype = i32
     lib.qkclip_rescale_mla.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32, vp, vp]
     lib.qkclip_rescale_mla.restype = i32
+    lib.attn_fwd_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_fwd_workspace_size.restype = sz
+    lib.attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
+    lib.attn_fwd.restype = i32
     lib.adamw_step.argtypes = [ctypes.POINTER(_AdamWTensor), i32, i32, ctypes.POINTER(_AdamWHParams), vp]
     lib.adamw_step.restype = i32
     lib.muon_status_string.argtypes = [i32]
@@ -336,6 +340,38 @@ def qkclip_rescale(Wq, Wk, s_max, d_head: int, tau: float = 100.0, alpha: float 
                               s_max.data_ptr(), tau, alpha, clipped.data_ptr(), _stream()),
            "qkclip_rescale")
     return clipped
+
+
+def attn_fwd(Q, K, V, logit_scale: float | None = None, causal: bool = True, out=None,
+             s_max=None, with_lse: bool = False, workspace=None):
+    """Softmax attention forward over bf16 [B, T, H, 128] tensors.  Returns
+    (O bf16 [B, T, H, 128], s_max fp32 [H], lse fp32 [B, H, T] or None);
+    s_max is the per-head maximum logit that QK-Clip takes."""
+    torch = _torch()
+    lib = load_library()
+    _need_cuda(Q, K, V)
+    if Q.dim() != 4 or Q.shape != K.shape or Q.shape != V.shape:
+        raise ValueError("Q, K and V must share a [B, T, H, d] shape")
+    for t in (Q, K, V):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("Q, K and V must be contiguous bfloat16")
+    B, T, H, D = Q.shape
+    if logit_scale is None:
+        logit_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(Q)
+    if out.shape != Q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of Q's shape")
+    if s_max is None:
+        s_max = torch.empty(H, dtype=torch.float32, device=Q.device)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=Q.device) if with_lse else None
+    need = int(lib.attn_fwd_workspace_size(B, T, H))
+    if workspace is None:
+        workspace = _workspace(need, Q.device)
+    _check(lib.attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), B, T, H, D, logit_scale, int(bool(causal)),
+                        out.data_ptr(), lse.data_ptr() if lse is not None else None, s_max.data_ptr(),
+                        workspace.data_ptr(), workspace.numel(), _stream()), "attn_fwd")
+    return out, s_max, lse
 
 
 def _flags(H, device, clipped):

@@ -562,6 +562,40 @@ int adamw_step(const adamw_tensor_t* tensors, int n_tensors, int dtype, const ad
   return MUON_OK;
 }
 
+size_t attn_fwd_workspace_size(int B, int T, int H) {
+  if (B < 1 || T < 1 || H < 1) return 0;
+  const int nqb = (T + 127) / 128;
+  return align_up(static_cast<size_t>(B) * H * nqb * 4 * sizeof(float));
+}
+
+int attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int T, int H, int d_head,
+             float logit_scale, int causal, uint16_t* O, float* lse, float* s_max, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+  if (!Q || !K || !V || !O || !s_max || B < 1 || T < 1 || H < 1) return MUON_ERR_INVALID_ARG;
+  if (d_head != 128) return MUON_ERR_UNSUPPORTED;
+  if (!(logit_scale > 0.0f) || !isfinite(logit_scale)) return MUON_ERR_INVALID_ARG;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16)) return MUON_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return MUON_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * T * H * d_head > (int64_t(1) << 40)) return MUON_ERR_INVALID_ARG;
+  const int nqb = (T + 127) / 128;
+  if (static_cast<int64_t>(B) * H * nqb > (int64_t(1) << 31) - 1) return MUON_ERR_INVALID_ARG;
+  const size_t need = attn_fwd_workspace_size(B, T, H);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return MUON_ERR_WORKSPACE;
+  AttnArgs A{};
+  A.Q = reinterpret_cast<const bf16_t*>(Q);
+  A.K = reinterpret_cast<const bf16_t*>(K);
+  A.V = reinterpret_cast<const bf16_t*>(V);
+  A.O = reinterpret_cast<bf16_t*>(O);
+  A.lse = lse;
+  A.partial = static_cast<float*>(workspace);
+  A.B = B; A.T = T; A.H = H; A.nqb = nqb;
+  A.scale = logit_scale;
+  A.c2 = static_cast<float>(static_cast<double>(logit_scale) * 1.4426950408889634);
+  MUON_LAUNCH(KIND_ATTN_FWD, stream, launch_attn_fwd(A, causal ? 1 : 0, stream));
+  MUON_LAUNCH(KIND_QK_REDUCE, stream, launch_qk_reduce(A.partial, B, H, nqb * 4, logit_scale, s_max, stream));
+  return MUON_OK;
+}
+
 int muon_profile_enable(int on) {
   for (auto& r : g_prof) {
     g_event_pool.push_back(r.a);
@@ -592,7 +626,7 @@ int muon_profile_collect(double* total_ms, int64_t* launches, int n_kinds) {
 const char* muon_kernel_kind_name(int kind) {
   static const char* names[KIND_COUNT] = {"momentum_norm", "norm_finalize", "ns_syrk_xxt", "ns_syrk_poly",
                                           "ns_gemm_bx",    "param_update",  "qk_rowmax",   "qk_reduce",
-                                          "qk_rescale",    "adamw"};
+                                          "qk_rescale",    "adamw",         "attn_fwd"};
   if (kind < 0 || kind >= KIND_COUNT) return "unknown";
   return names[kind];
 }

@@ -67,7 +67,8 @@ enum KernelKind {
   KIND_QK_REDUCE = 7,
   KIND_QK_RESCALE = 8,
   KIND_ADAMW = 9,
-  KIND_COUNT = 10
+  KIND_ATTN_FWD = 10,
+  KIND_COUNT = 11
 };
 
 // ---------------------------------------------------------------------------
@@ -185,6 +186,21 @@ struct RescaleLaunch {
 };
 hipError_t launch_qk_rescale(const RescaleLaunch& L, int dtype, int H, const float* s_max, float tau,
                              int32_t* clipped, hipStream_t s);
+
+// Causal softmax attention forward (head dimension 128) that also writes
+// one maximum raw logit per (batch row, head, query block, wave) to partial.
+struct AttnArgs {
+  const bf16_t* Q;
+  const bf16_t* K;
+  const bf16_t* V;
+  bf16_t* O;
+  float* lse;       // optional [B][H][T]
+  float* partial;   // [B][H][nqb][4]
+  int B, T, H, nqb;
+  float scale;      // logit scale (1/sqrt(d))
+  float c2;         // scale * log2(e)
+};
+hipError_t launch_attn_fwd(const AttnArgs& A, int causal, hipStream_t s);
 
 // Multi-tensor AdamW: block b of a launch works on tensor t with
 // blk_start[t] <= b < blk_start[t + 1], elements (b - blk_start[t]) * 2048 ...

@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["muon_step", "ns_orthogonalize", "qkclip_rowmax", "qkclip_rescale",
-              "qkclip_rescale_slices", "qkclip_rescale_mla", "adamw_step"]:
+              "qkclip_rescale_slices", "qkclip_rescale_mla", "adamw_step", "attn_fwd"]:
         assert n in names
 
 
@@ -96,6 +96,11 @@ def test_host_validation_without_gpu(lib):
     assert lib.adamw_step(t, 1, 1, ctypes.byref(hp), None) == mm.MUON_ERR_INVALID_ARG
     t[0] = mm._AdamWTensor(17, 16, 16, 16, 10)
     assert lib.adamw_step(t, 1, 1, ctypes.byref(hp), None) == mm.MUON_ERR_INVALID_ARG
+    # attention forward: head dim other than 128, missing output, no workspace
+    assert lib.attn_fwd(16, 16, 16, 1, 8, 2, 64, 0.1, 1, 16, None, 16, 16, 1 << 20, None) == mm.MUON_ERR_UNSUPPORTED
+    assert lib.attn_fwd(16, 16, 16, 1, 8, 2, 128, 0.1, 1, None, None, 16, 16, 1 << 20, None) == mm.MUON_ERR_INVALID_ARG
+    assert lib.attn_fwd(16, 16, 16, 1, 8, 2, 128, 0.1, 1, 16, None, 16, None, 0, None) == mm.MUON_ERR_WORKSPACE
+    assert lib.attn_fwd_workspace_size(2, 300, 3) >= 2 * 3 * 3 * 4 * 4   # [B][H][query blocks][4 waves] fp32
     # nothing to do is not an error and launches nothing
     assert lib.adamw_step(t, 0, 1, ctypes.byref(hp), None) == mm.MUON_OK
     assert lib.ns_workspace_size(1, 0, 4) == 0
