@@ -226,6 +226,7 @@ def main():
     }
 
     out["companion"] = companion(mm, torch, dev, seed, n_mats * m * n)
+    out["companion"]["attn_fwd"] = attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, prof["qk_rowmax"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
     print(json.dumps(out), flush=True)
@@ -259,6 +260,34 @@ def blas_reference(torch, reps=10):
         ms = e0.elapsed_time(e1) / reps
         res[name] = {"ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 1)}
     res["ns_iteration_ms"] = round(sum(v["ms"] for k, v in res.items() if isinstance(v, dict)), 3)
+    return res
+
+
+def attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, rowmax_prof, reps=5):
+    """The causal attention forward on the layer's Q, K and a synthetic V,
+    which produces the same S_max as the separate rowmax pass.  Algorithmic
+    work: two products over the causal pairs, 4 d B H T (T + 1) / 2 flops."""
+    from synthetic import generators as gen
+    V = gen.bulk_normal_torch((B, T, H, D), 1.0, seed + 40, dev, torch.bfloat16)
+    out = torch.empty_like(Q)
+    s_max = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(mm.load_library().attn_fwd_workspace_size(B, T, H), 256), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    mm.attn_fwd(Q, K, V, scale, True, out=out, s_max=s_max, workspace=ws)
+    torch.cuda.synchronize()
+    mm.profile_enable(True)
+    for _ in range(reps):
+        mm.attn_fwd(Q, K, V, scale, True, out=out, s_max=s_max, workspace=ws)
+    prof = mm.profile_collect()
+    mm.profile_enable(False)
+    ms, cnt = prof["attn_fwd"]
+    t = ms / cnt * 1e-3
+    flop = 4.0 * D * B * H * T * (T + 1) / 2
+    res = {"avg_us": round(1e6 * t, 1), "tflops": round(flop / t / 1e12, 1),
+           "frac_mfma_peak": round(flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if rowmax_prof[1]:
+        res["separate_rowmax_pass_us"] = round(1e3 * rowmax_prof[0] / rowmax_prof[1], 1)
+    del V, out
     return res
 
 
