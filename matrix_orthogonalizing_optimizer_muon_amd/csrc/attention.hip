@@ -25,6 +25,9 @@ namespace muon {
 
 namespace {
 
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kD = 128;        // head dimension
 constexpr int kQB = 128;       // queries per block
 constexpr int kKB = 64;        // keys per iteration
@@ -41,10 +44,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][kKB * kKP];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][kD * kVP];
 
-  const int BH = A.B * A.H;
-  const int lin = blockIdx.x;
-  const int qb = A.nqb - 1 - lin / BH;      // longest causal rows first
-  const int bh = lin - (lin / BH) * BH;
+  // each XCD walks a contiguous range of (head, query block) pairs, one head's
+  // query blocks back to back (longest causal rows first), so a head's K and V
+  // are fetched into that XCD's L2 once
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / A.nqb;
+  const int qb = A.nqb - 1 - (lin - bh * A.nqb);
   const int b = bh / A.H, head = bh - b * A.H;
   const int T = A.T;
   const int64_t tok = static_cast<int64_t>(A.H) * kD;                 // token stride
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     const float m_new = fmaxf(m_run, mloc);
     float alpha = 1.0f, mc = 0.0f;
     if (m_new != -INFINITY) {
-      alpha = exp2f((m_run - m_new) * c2);
+      alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       mc = m_new * c2;
     }
     m_run = m_new;
@@ -154,18 +159,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     bf16x8_t pb[4];
     static_for<32>([&](auto i) {
       constexpr int MB = decltype(i)::value / 16, E = decltype(i)::value % 16;
-      const float p = exp2f(fmaf(s[MB][E], c2, -mc));
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[MB][E], c2, -mc));
       l_run += p;
       s[MB][E] = p;
     });
     static_for<4>([&](auto cc) {
       constexpr int C = decltype(cc)::value;
-      u32x4_t w;
-      static_for<4>([&](auto j) {
+      f32x8_t pv;
+      static_for<8>([&](auto j) {
         constexpr int J = decltype(j)::value;
-        w[J] = pack2_bf16(s[C / 2][8 * (C % 2) + 2 * J], s[C / 2][8 * (C % 2) + 2 * J + 1]);
+        pv[J] = s[C / 2][8 * (C % 2) + J];
       });
-      pb[C] = __builtin_bit_cast(bf16x8_t, w);
+      pb[C] = __builtin_convertvector(pv, bf16x8_t);   // v_cvt_pk_bf16_f32: nearest-even
     });
     // O^T += V^T P^T; slot j of lane half hf is key 16 c + 8 (j / 4) + 4 hf + j % 4
     static_for<4>([&](auto cc) {
@@ -205,8 +210,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
         const int d0 = 32 * db + 8 * G + 4 * hf;
         u32x2_t pk;
         constexpr int DB = decltype(db)::value;
-        pk[0] = pack2_bf16(o[DB][4 * G] * inv, o[DB][4 * G + 1] * inv);
-        pk[1] = pack2_bf16(o[DB][4 * G + 2] * inv, o[DB][4 * G + 3] * inv);
+        const f32x4_t ov = {o[DB][4 * G] * inv, o[DB][4 * G + 1] * inv, o[DB][4 * G + 2] * inv,
+                            o[DB][4 * G + 3] * inv};
+        pk = __builtin_bit_cast(u32x2_t, __builtin_convertvector(ov, bf16x4_t));
         *reinterpret_cast<u32x2_t*>(orow + d0) = pk;
       });
     });
