@@ -94,10 +94,16 @@ def main():
         src.fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(3):
             dst.copy_(src)
+        e1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 3}))
+        ms = e0.elapsed_time(e1) / 3
+        print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 3,
+                          "copy_GBs_read_plus_write": round(2 * src.numel() / ms / 1e6, 1)}))
         return
 
     if args.blas_reference:
@@ -227,6 +233,8 @@ def main():
 
     out["companion"] = companion(mm, torch, dev, seed, n_mats * m * n)
     out["companion"]["attn_fwd"] = attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, prof["qk_rowmax"])
+    del Q, K, Wqkv, Wo, Gqkv, Go, Mqkv, Mo, ws, groups
+    out["layer_hidden2048"] = layer_hidden2048(mm, torch, dev, seed, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
     print(json.dumps(out), flush=True)
@@ -261,6 +269,47 @@ def blas_reference(torch, reps=10):
         res[name] = {"ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 1)}
     res["ns_iteration_ms"] = round(sum(v["ms"] for k, v in res.items() if isinstance(v, dict)), 3)
     return res
+
+
+def layer_hidden2048(mm, torch, dev, seed, steps, warmup):
+    """The Muon step alone (no QK-Clip) on one transformer layer of hidden
+    2048: W_q, W_k, W_v, W_o 2048x2048, MLP up/gate 8192x2048, down 2048x8192,
+    bf16 params and low-rank-plus-noise grads, fp32 momentum.  A second
+    reading of the same metric; the headline line is the MuonClip layer,
+    whose step is the only one that covers every stage of the path."""
+    from synthetic import generators as gen
+    wl = gen.workload(2)
+    groups = []
+    for gi, gr in enumerate(wl.groups):
+        W = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.02, seed + 100 + gi, dev, torch.bfloat16)
+        G = torch.stack([gen.lowrank_torch(gr.rows, gr.cols, seed + 200 + 10 * gi + b, dev)
+                         for b in range(gr.batch)])
+        M = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.5, seed + 300 + gi, dev, torch.float32)
+        groups.append((W, G, M))
+    hp = mm.HParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=True,
+                    ns_steps=wl.ns_steps, ns_coeffs=wl.ns_coeffs, ns_eps=wl.ns_eps, rms_target=wl.rms_target)
+    ws = torch.empty(mm.workspace_size(groups), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        mm.muon_step(groups, hp, workspace=ws)
+    torch.cuda.synchronize()
+    mm.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mm.muon_step(groups, hp, workspace=ws)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    prof = mm.profile_collect()
+    mm.profile_enable(False)
+    flop = 0.0
+    for gr in wl.groups:
+        m, n = min(gr.rows, gr.cols), max(gr.rows, gr.cols)
+        flop += gr.batch * wl.ns_steps * sum(ns_flops(m, n).values())
+    ns_ms = sum(prof[k][0] for k in ("ns_syrk_xxt", "ns_syrk_poly", "ns_gemm_bx")) / steps
+    return {"workload": "one layer, hidden 2048: 4 x 2048x2048, 2 x 8192x2048, 1 x 2048x8192",
+            "steps_per_s": round(steps / el, 2), "ms_per_step": round(1e3 * el / steps, 3),
+            "ns_tflops": round(flop / (ns_ms * 1e-3) / 1e12, 1),
+            "ns_frac_mfma_peak": round(flop / (ns_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernels_ms_per_step": {k: round(v[0] / steps, 4) for k, v in prof.items() if v[1]}}
 
 
 def attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, rowmax_prof, reps=5):
