@@ -239,7 +239,8 @@ GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b,
   const int64_t sx = static_cast<int64_t>(p.mp) * p.np, sa = static_cast<int64_t>(p.mp) * p.mp;
   const int T = p.mp / p.tile;
   q.alpha = at<float>(ws, p.off_inv);
-  q.ct_vec = 1;
+  q.c16 = 1;
+  q.ct16 = 1;
   if (stage == STAGE_SYRK) {
     q.P = X; q.Q = X; q.sP = sx; q.sQ = sx; q.ldp = p.np; q.ldq = p.np; q.K = p.np;
     q.C = A; q.Ct = A; q.sC = sa; q.sCt = sa; q.ldc = p.mp; q.ldct = p.mp;
@@ -273,11 +274,9 @@ GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b,
     } else if (fin && fin->ptr) {
       // write the result straight into the caller's dense output
       q.mvalid = p.m; q.nvalid = p.n;
-      if (!p.tall) { q.C = fin->ptr; q.sC = fin->stride; q.ldc = fin->ld; }
-      else {
-        q.Ct = fin->ptr; q.sCt = fin->stride; q.ldct = fin->ld;
-        q.ct_vec = (fin->ld % 4 == 0) && aligned(fin->ptr, 8) && (fin->stride % 4 == 0);
-      }
+      const int v16 = (fin->ld % 8 == 0) && aligned(fin->ptr, 16) && (fin->stride % 8 == 0);
+      if (!p.tall) { q.C = fin->ptr; q.sC = fin->stride; q.ldc = fin->ld; q.c16 = v16; }
+      else { q.Ct = fin->ptr; q.sCt = fin->stride; q.ldct = fin->ld; q.ct16 = v16; }
     } else {
       q.mvalid = p.mp; q.nvalid = p.np;
       if (!p.tall) { q.C = Xn; q.sC = sx; q.ldc = p.np; }

@@ -95,7 +95,7 @@ struct GemmProb {
   int sym;          // 1: only tiles ti <= tj, written at (ti,tj) and mirrored
   int alpha_pow;    // 0: s = 1, 1: s = alpha, 2: s = alpha^2
   int mvalid, nvalid;  // outputs are written only for i < mvalid, j < nvalid
-  int ct_vec;       // 1 if Ct rows allow aligned 8-byte stores
+  int c16, ct16;    // 1 if C / Ct rows allow aligned 16-byte stores
   float c_acc, c_e;
   float c_diag;     // added on the diagonal i == j (before the scale s)
 };

@@ -29,63 +29,78 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kPitch = kBK + 8;  // padded LDS row (bf16): 144 bytes, conflict-free b128 reads
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Output values of one lane for MFMA block (A, B), row group Qd: four
+// consecutive rows i0 + 32 A + 8 Qd + (0..3) of column j0 + 32 B, as fp32
+//   v = ca * acc + [i == j] cd + ce * Et[j][i]
+// rounded once to bf16 (v_cvt_pk_bf16_f32, nearest-even), two per dword.
 struct EpiArgs {
   float ca, ce, cd;
-  bf16_t* C;
-  bf16_t* Ct;
-  const bf16_t* Et;
-  int ldc, ldct, lde, mvalid, nvalid, ct_vec;
-  int i0, j0;  // this lane's first row and its column inside block (0, 0)
+  const bf16_t* Et;   // staged Et tile in LDS (row pitch lde), or null
+  int lde;
+  int gi0, gj0;       // this lane's first row / column in the matrix (block (0, 0))
+  int li0, lj0;       // the same inside the tile
 };
 
-// Epilogue of one 32x32 MFMA block (a, b): four groups of four consecutive
-// rows per lane.  Compile-time block indices keep the accumulators in
-// registers.
-template <int A, int B>
-__device__ __forceinline__ void epilogue_block(const f32x16_t& acc, const EpiArgs& e) {
-  const int j = e.j0 + 32 * B;
-  if (j >= e.nvalid) return;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = e.i0 + 32 * A + 8 * q;
-    float v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = e.ca * acc[4 * q + r] + ((i + r == j) ? e.cd : 0.0f);
-    if (e.Et) {
-      const uint2 ev = *reinterpret_cast<const uint2*>(e.Et + static_cast<int64_t>(j) * e.lde + i);
-      v[0] = fmaf(e.ce, bf16_to_f32(ev.x & 0xffff), v[0]);
-      v[1] = fmaf(e.ce, bf16_to_f32(ev.x >> 16), v[1]);
-      v[2] = fmaf(e.ce, bf16_to_f32(ev.y & 0xffff), v[2]);
-      v[3] = fmaf(e.ce, bf16_to_f32(ev.y >> 16), v[3]);
-    }
-    bf16_t o[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16(v[r]);
-    if (e.C) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (i + r < e.mvalid) e.C[static_cast<int64_t>(i + r) * e.ldc + j] = o[r];
-    }
-    if (e.Ct) {
-      bf16_t* dst = e.Ct + static_cast<int64_t>(j) * e.ldct + i;
-      if (e.ct_vec && i + 3 < e.mvalid) {
-        uint2 pk;
-        pk.x = static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16);
-        pk.y = static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = pk;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (i + r < e.mvalid) dst[r] = o[r];
-      }
-    }
+template <int A, int B, int Qd>
+__device__ __forceinline__ u32x2_t epi_quad(const f32x16_t& acc, const EpiArgs& e) {
+  const int i = e.gi0 + 32 * A + 8 * Qd;
+  const int j = e.gj0 + 32 * B;
+  f32x4_t v;
+  static_for<4>([&](auto r) {
+    constexpr int R = decltype(r)::value;
+    v[R] = e.ca * acc[4 * Qd + R] + ((i + R == j) ? e.cd : 0.0f);
+  });
+  if (e.Et) {
+    // the Et tile staged in LDS, layout [j][i]
+    const u32x2_t ev = *reinterpret_cast<const u32x2_t*>(e.Et + (e.lj0 + 32 * B) * e.lde + e.li0 + 32 * A + 8 * Qd);
+    v[0] = fmaf(e.ce, bf16_to_f32(ev[0] & 0xffff), v[0]);
+    v[1] = fmaf(e.ce, bf16_to_f32(ev[0] >> 16), v[1]);
+    v[2] = fmaf(e.ce, bf16_to_f32(ev[1] & 0xffff), v[2]);
+    v[3] = fmaf(e.ce, bf16_to_f32(ev[1] >> 16), v[3]);
   }
+  return __builtin_bit_cast(u32x2_t, __builtin_convertvector(v, bf16x4_t));
 }
 
-template <int F, int G, int... Is>
-__device__ __forceinline__ void epilogue_all(const f32x16_t (&acc)[F][G], const EpiArgs& e,
-                                             std::integer_sequence<int, Is...>) {
-  (epilogue_block<Is / G, Is % G>(acc[Is / G][Is % G], e), ...);
+// Stage the TILE x TILE tile src[r0 + r][c0 + c] (leading dimension ld) in
+// LDS with row pitch EP.  The caller guarantees the whole tile lies inside
+// src (the epilogue's E operand is always a padded workspace matrix).
+template <int TILE, int EP, int NT>
+__device__ __forceinline__ void copy_in(bf16_t* st, const bf16_t* src, int ld, int r0, int c0, int tid) {
+  constexpr int CPRW = TILE / 8;
+  constexpr int N = TILE * CPRW / NT;
+  static_for<N>([&](auto k) {
+    const int c = tid + NT * decltype(k)::value;
+    const int row = c / CPRW, cc = (c % CPRW) * 8;
+    *reinterpret_cast<u32x4_t*>(st + row * EP + cc) =
+        *reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(r0 + row) * ld + c0 + cc);
+  });
+}
+
+// Copy a TILE x TILE bf16 tile staged in LDS (row pitch EP elements) to
+// dst[r][c] (leading dimension ld), rows < rvalid - r0, cols < cvalid - c0,
+// 16 bytes per store where the chunk is whole and aligned.
+template <int TILE, int EP, int NT>
+__device__ __forceinline__ void copy_out(const bf16_t* st, bf16_t* dst, int ld, int r0, int c0, int rvalid,
+                                         int cvalid, bool vec16, int tid) {
+  constexpr int CPRW = TILE / 8;
+  constexpr int N = TILE * CPRW / NT;
+#pragma unroll 4
+  for (int k = 0; k < N; ++k) {
+    const int c = tid + NT * k;
+    const int row = c / CPRW, cc = (c % CPRW) * 8;
+    const int gr = r0 + row, gc = c0 + cc;
+    if (gr >= rvalid || gc >= cvalid) continue;
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(st + row * EP + cc);
+    bf16_t* d = dst + static_cast<int64_t>(gr) * ld + gc;
+    if (vec16 && gc + 7 < cvalid) {
+      *reinterpret_cast<u32x4_t*>(d) = w;
+    } else {
+      for (int q = 0; q < 8 && gc + q < cvalid; ++q)
+        d[q] = static_cast<bf16_t>((w[q >> 1] >> (16 * (q & 1))) & 0xffff);
+    }
+  }
 }
 
 template <int TILE, int STAGE>
@@ -101,8 +116,10 @@ void ns_gemm_kernel(GemmLaunch L) {
   constexpr int NCH = TILE / RPP;     // passes (chunks per thread per operand)
   static_assert(TILE % RPP == 0, "staging map must cover the tile exactly");
 
-  __shared__ __attribute__((aligned(16))) bf16_t sP[2][TILE * kPitch];
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][TILE * kPitch];
+  // two stages of the P and Q slices; the epilogue reuses the whole buffer
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * TILE * kPitch];
+  auto sP = [&](int buf) { return smem + buf * TILE * kPitch; };
+  auto sQ = [&](int buf) { return smem + (2 + buf) * TILE * kPitch; };
 
   // ---- block -> (problem, matrix, tile)
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -185,8 +202,8 @@ void ns_gemm_kernel(GemmLaunch L) {
     });
   };
   auto sstore = [&](int buf) {
-    char* bP = reinterpret_cast<char*>(sP[buf]) + sOff;
-    char* bQ = reinterpret_cast<char*>(sQ[buf]) + sOff;
+    char* bP = reinterpret_cast<char*>(sP(buf)) + sOff;
+    char* bQ = reinterpret_cast<char*>(sQ(buf)) + sOff;
     static_for<NCH>([&](auto c) {
       *reinterpret_cast<u32x4_t*>(bP + c * RPP * kPitch * 2) = rP[c];
       *reinterpret_cast<u32x4_t*>(bQ + c * RPP * kPitch * 2) = rQ[c];
@@ -208,8 +225,8 @@ void ns_gemm_kernel(GemmLaunch L) {
   const int boff = ((wc0 + frow) * kPitch + fk) * 2;
   bf16x8_t fa[2][F], fb[2][G];
   auto read_frags = [&](int buf, int s, auto slot) {
-    const char* bP = reinterpret_cast<const char*>(sP[buf]) + aoff + s * 32;
-    const char* bQ = reinterpret_cast<const char*>(sQ[buf]) + boff + s * 32;
+    const char* bP = reinterpret_cast<const char*>(sP(buf)) + aoff + s * 32;
+    const char* bQ = reinterpret_cast<const char*>(sQ(buf)) + boff + s * 32;
     static_for<F>([&](auto a) { fa[slot][a] = *reinterpret_cast<const bf16x8_t*>(bP + a * 32 * kPitch * 2); });
     static_for<G>([&](auto b) { fb[slot][b] = *reinterpret_cast<const bf16x8_t*>(bQ + b * 32 * kPitch * 2); });
   };
@@ -258,23 +275,78 @@ void ns_gemm_kernel(GemmLaunch L) {
   // ---- epilogue.  Element e of acc[a][b] holds C[i][j] with
   //   i = tile_i0 + wr0 + 32 a + 8 (e / 4) + 4 (lane / 32) + (e % 4),
   //   j = tile_j0 + wc0 + 32 b + (lane % 32).
+  // The rounded tile goes through LDS so both layouts leave in 16-byte
+  // stores of whole rows (direct stores from this layout would be 2- or
+  // 8-byte pieces of many cache lines).
   float sc = 1.0f;
   if (p.alpha_pow) {
     const float al = p.alpha[mat];
     sc = (p.alpha_pow == 2) ? al * al : al;
   }
+  constexpr int EP = TILE + 8;                 // staged tile row pitch (bf16)
+  static_assert(TILE * EP <= 4 * TILE * kPitch, "staged tile must fit the LDS buffer");
   EpiArgs e;
   e.ca = p.c_acc * sc;
   e.ce = p.c_e * sc;
   e.cd = p.c_diag * sc;
-  e.C = p.C ? p.C + mat * p.sC : nullptr;
-  e.Ct = (p.Ct && (!p.sym || ti != tj)) ? p.Ct + mat * p.sCt : nullptr;
-  e.Et = p.Et ? p.Et + mat * p.sEt : nullptr;
-  e.ldc = p.ldc; e.ldct = p.ldct; e.lde = p.lde;
-  e.mvalid = p.mvalid; e.nvalid = p.nvalid; e.ct_vec = p.ct_vec;
-  e.i0 = ti * TILE + wr0 + 4 * (lane >> 5);
-  e.j0 = tj * TILE + wc0 + (lane & 31);
-  epilogue_all<F, G>(acc, e, std::make_integer_sequence<int, F * G>{});
+  e.Et = nullptr;
+  e.lde = EP;
+  e.gi0 = ti * TILE + wr0 + 4 * (lane >> 5);
+  e.gj0 = tj * TILE + wc0 + (lane & 31);
+  e.li0 = wr0 + 4 * (lane >> 5);
+  e.lj0 = wc0 + (lane & 31);
+  bf16_t* C = p.C ? p.C + mat * p.sC : nullptr;
+  bf16_t* Ct = (p.Ct && (!p.sym || ti != tj)) ? p.Ct + mat * p.sCt : nullptr;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();                // every wave is done with the K slices
+  if (p.Et) {
+    // E[j][i] tile (the transposed layout of this output tile), coalesced into LDS
+    copy_in<TILE, EP, NT>(smem, p.Et + mat * p.sEt, p.lde, tj * TILE, ti * TILE, tid);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    e.Et = smem;
+  }
+  u32x2_t quad[F][G][4];
+  static_for<F * G * 4>([&](auto x) {
+    constexpr int X = decltype(x)::value;
+    constexpr int A = X / (4 * G), B = (X / 4) % G, Qd = X % 4;
+    quad[A][B][Qd] = epi_quad<A, B, Qd>(acc[A][B], e);
+  });
+  const int li0 = e.li0;                       // local row of quad (0, 0, 0)
+  const int lj0 = e.lj0;                       // local column of block (., 0)
+  if (p.Et) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();              // the staged E tile is read; reuse the buffer
+  }
+  if (Ct) {
+    // transposed layout [j][i]: each quad is 4 consecutive i of one j
+    static_for<F * G * 4>([&](auto x) {
+      constexpr int X = decltype(x)::value;
+      constexpr int A = X / (4 * G), B = (X / 4) % G, Qd = X % 4;
+      *reinterpret_cast<u32x2_t*>(smem + (lj0 + 32 * B) * EP + li0 + 32 * A + 8 * Qd) = quad[A][B][Qd];
+    });
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    copy_out<TILE, EP, NT>(smem, Ct, p.ldct, tj * TILE, ti * TILE, p.nvalid, p.mvalid, p.ct16 != 0, tid);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (C) {
+    // row-major layout [i][j]
+    static_for<F * G * 4>([&](auto x) {
+      constexpr int X = decltype(x)::value;
+      constexpr int A = X / (4 * G), B = (X / 4) % G, Qd = X % 4;
+      bf16_t* d = smem + (li0 + 32 * A + 8 * Qd) * EP + lj0 + 32 * B;
+      const u32x2_t w = quad[A][B][Qd];
+      d[0] = static_cast<bf16_t>(w[0] & 0xffff);
+      d[EP] = static_cast<bf16_t>(w[0] >> 16);
+      d[2 * EP] = static_cast<bf16_t>(w[1] & 0xffff);
+      d[3 * EP] = static_cast<bf16_t>(w[1] >> 16);
+    });
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    copy_out<TILE, EP, NT>(smem, C, p.ldc, ti * TILE, tj * TILE, p.mvalid, p.nvalid, p.c16 != 0, tid);
+  }
 }
 
 }  // namespace
