@@ -65,7 +65,9 @@ def ns_tolerance(rows, cols):
     return 2e-2 if min(rows, cols) >= 8 else 5e-2
 
 
-NS_SHAPES = [(96, 160), (200, 72), (128, 128), (1, 37), (37, 1), (300, 600), (640, 520), (520, 1100)]
+NS_SHAPES = [(96, 160), (200, 72), (128, 128), (1, 37), (37, 1), (300, 600), (640, 520), (520, 1100),
+             # long contractions over few output tiles (K up to 16 x the tile rows)
+             (300, 2100), (4096, 256), (512, 2048)]
 
 
 @pytest.mark.parametrize("shape", NS_SHAPES)
