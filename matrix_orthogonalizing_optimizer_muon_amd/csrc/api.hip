@@ -305,6 +305,10 @@ int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c,
         }
         if (L.nprob == 0) continue;
         L.prefix[L.nprob] = tiles;
+        // column bands per XCD when every problem of a B X launch allows them
+        L.band = (stage == STAGE_BX) ? 1 : 0;
+        for (int k = 0; k < L.nprob; ++k)
+          if (L.p[k].tn % 8 != 0) L.band = 0;
         MUON_LAUNCH(kinds[stage], s, launch_ns_gemm(L, tile, stage, tiles, s));
       }
     }

@@ -102,6 +102,7 @@ struct GemmProb {
 
 struct GemmLaunch {
   int nprob;
+  int band;         // non-symmetric products with tn % 8 == 0: column bands per XCD
   int prefix[kMaxProbs + 1];
   GemmProb p[kMaxProbs];
 };

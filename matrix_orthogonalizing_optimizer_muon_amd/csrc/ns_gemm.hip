@@ -122,15 +122,31 @@ void ns_gemm_kernel(GemmLaunch L) {
   auto sQ = [&](int buf) { return smem + (2 + buf) * TILE * kPitch; };
 
   // ---- block -> (problem, matrix, tile)
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = L.band ? static_cast<int>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
   int gi = 0;
   while (gi + 1 < L.nprob && lin >= L.prefix[gi + 1]) ++gi;
   const GemmProb& p = L.p[gi];
   const int local = lin - L.prefix[gi];
-  const int mat = local / p.tiles_per_mat;
+  int mat = local / p.tiles_per_mat;
   int t = local - mat * p.tiles_per_mat;
   int ti, tj;
-  if (p.sym) {
+  if (L.band) {
+    // Column bands: block i runs on XCD x = i % 8, which owns columns
+    // [x tn/8, (x+1) tn/8) of every matrix; every XCD walks the same 8-row
+    // group at the same time (each problem's block range starts at a
+    // multiple of 8), so the row panels they share come from the
+    // memory-side cache rather than HBM.  Inside a group, column-major.
+    const int x = local & 7, w = local >> 3;
+    const int bw = p.tn / 8;
+    const int per = p.tm * bw;
+    mat = w / per;
+    const int u = w - mat * per;
+    const int g8 = u / (8 * bw);
+    const int rows = min(8, p.tm - 8 * g8);
+    const int v = u - g8 * 8 * bw;
+    ti = 8 * g8 + v % rows;
+    tj = x * bw + v / rows;
+  } else if (p.sym) {
     {
       constexpr int SB = 8;
       // super-blocks of SB x SB tiles over the upper triangle, row-major over
