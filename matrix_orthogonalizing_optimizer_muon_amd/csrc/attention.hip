@@ -134,18 +134,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     // key of accumulator element e of block mb: k0 + 32 mb + 8 (e / 4) + 4 hf + e % 4
     const bool need_mask = (k0 + kKB > T) || (CAUSAL && k0 + kKB - 1 > q0w);
     float mloc = -INFINITY;
-    static_for<32>([&](auto i) {
-      constexpr int MB = decltype(i)::value / 16, E = decltype(i)::value % 16;
-      float v = s[MB][E];
-      if (need_mask) {
+    if (need_mask) {
+      static_for<32>([&](auto i) {
+        constexpr int MB = decltype(i)::value / 16, E = decltype(i)::value % 16;
         const int key = k0 + 32 * MB + 8 * (E / 4) + 4 * hf + (E % 4);
         const bool ok = key < T && (!CAUSAL || key <= q);
-        v = ok ? v : -INFINITY;
-        s[MB][E] = v;
-      }
-      nanf |= (v != v);
-      mloc = fmaxf(mloc, v);
+        s[MB][E] = ok ? s[MB][E] : -INFINITY;
+      });
+    }
+    // IEEE maximum propagates NaN (v_maximum3_f32: two logits per instruction)
+    static_for<16>([&](auto i) {
+      constexpr int MB = decltype(i)::value / 8, E = 2 * (decltype(i)::value % 8);
+      mloc = __builtin_elementwise_maximum(mloc, __builtin_elementwise_maximum(s[MB][E], s[MB][E + 1]));
     });
+    nanf |= (mloc != mloc);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float m_new = fmaxf(m_run, mloc);
     float alpha = 1.0f, mc = 0.0f;

@@ -98,7 +98,6 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   };
 
   float m = -INFINITY;
-  int has_nan = 0;
 
   gload(0);
   sstore(0);
@@ -124,14 +123,13 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         });
       });
       const bool full = (!causal || c0 + KB - 1 <= r0) && (r0 + 63 < T) && (c0 + KB - 1 < T);
+      // IEEE maximum propagates NaN (v_maximum3_f32: two logits per instruction)
       if (full) {
         static_for<2 * NB>([&](auto ab) {
           constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
-          static_for<16>([&](auto e) {
-            constexpr int E = decltype(e)::value;
-            const float v = acc[A][N][E];
-            m = fmaxf(m, v);
-            has_nan |= (v != v);
+          static_for<8>([&](auto e) {
+            constexpr int E = 2 * decltype(e)::value;
+            m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(acc[A][N][E], acc[A][N][E + 1]));
           });
         });
       } else {
@@ -140,12 +138,9 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
           const int j = c0 + N * 32 + (lane & 31);
           static_for<16>([&](auto e) {
             constexpr int E = decltype(e)::value;
-            const float v = acc[A][N][E];
             const int i = r0 + A * 32 + 8 * (E / 4) + 4 * (lane >> 5) + (E % 4);
-            if (i < T && j < T && (!causal || j <= i)) {
-              m = fmaxf(m, v);
-              has_nan |= (v != v);
-            }
+            const bool ok = i < T && j < T && (!causal || j <= i);
+            m = __builtin_elementwise_maximum(m, ok ? acc[A][N][E] : -INFINITY);
           });
         });
       }
@@ -154,8 +149,8 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     barrier();
   }
 
+  const int has_nan = __any(m != m) ? 1 : 0;
   m = wave_max(m);
-  has_nan = __any(has_nan) ? 1 : 0;
   if (lane == 0) {
     wmax[wave] = m;
     wnan[wave] = has_nan;
