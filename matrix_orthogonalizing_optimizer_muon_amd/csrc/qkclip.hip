@@ -79,17 +79,23 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   const int nkb = (kend + KB - 1) / KB;
 
   const int lrow = tid / CPR, lcol = (tid % CPR) * 8;
-  u32x4_t rk[NCH];
-  auto gload = [&](int kb) {
+  // NS register sets: key block kb + NS is loaded while kb computes; with two
+  // sets, kb + 1 waits in the other one for the LDS buffer kb leaves (one set
+  // for d = 256, whose query fragments take the registers)
+  constexpr int NS = (D <= 128) ? 2 : 1;
+  u32x4_t rk[NS][NCH];
+  auto gload = [&](int kb, auto set) {
+    constexpr int SET = decltype(set)::value;
     static_for<NCH>([&](auto c) {
       const int j = kb * KB + lrow + c * RPP;
-      if (j < T) rk[c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + lcol);
-      else rk[c] = u32x4_t{};
+      if (j < T) rk[SET][c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + lcol);
+      else rk[SET][c] = u32x4_t{};
     });
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, auto set) {
+    constexpr int SET = decltype(set)::value;
     static_for<NCH>([&](auto c) {
-      *reinterpret_cast<u32x4_t*>(&sK[buf][(lrow + c * RPP) * PITCH + lcol]) = rk[c];
+      *reinterpret_cast<u32x4_t*>(&sK[buf][(lrow + c * RPP) * PITCH + lcol]) = rk[SET][c];
     });
   };
   auto barrier = [&]() {
@@ -99,27 +105,42 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 
   float m = -INFINITY;
 
-  gload(0);
-  sstore(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  gload(0, S0{});
+  if constexpr (NS == 2) {
+    if (nkb > 1) gload(1, S1{});
+  }
+  sstore(0, S0{});
   barrier();
-  for (int kb = 0; kb < nkb; ++kb) {
+  auto body = [&](int kb, auto par) {
+    constexpr int P = decltype(par)::value;
+    constexpr int LS = (NS == 2) ? P : 0;          // set receiving block kb + NS
+    constexpr int SS = (NS == 2) ? (P ^ 1) : 0;    // set holding block kb + 1
     const int cur = kb & 1;
     const bool more = kb + 1 < nkb;
-    if (more) gload(kb + 1);
+    if (kb + NS < nkb) gload(kb + NS, std::integral_constant<int, LS>{});
     const int c0 = kb * KB;
     const bool any = (r0 < T) && (!causal || c0 <= r0 + 63);
     if (any) {
       f32x16_t acc[2][NB];
       static_for<2 * NB>([&](auto ab) { acc[ab / NB][ab % NB] = f32x16_t{}; });
       const bf16_t* sKc = sK[cur];
-      static_for<KS>([&](auto s) {
-        bf16x8_t kf[NB];
+      // K fragments double-buffered: substep s + 1 is read while s multiplies
+      bf16x8_t kf[2][NB];
+      auto read_kf = [&](auto sub) {
+        constexpr int SUB = decltype(sub)::value;
         static_for<NB>([&](auto n) {
-          kf[n] = *reinterpret_cast<const bf16x8_t*>(&sKc[(n * 32 + frow) * PITCH + s * 16 + fk]);
+          kf[SUB & 1][n] = *reinterpret_cast<const bf16x8_t*>(&sKc[(n * 32 + frow) * PITCH + SUB * 16 + fk]);
         });
+      };
+      read_kf(std::integral_constant<int, 0>{});
+      static_for<KS>([&](auto s) {
+        constexpr int SS = decltype(s)::value;
+        if constexpr (SS + 1 < KS) read_kf(std::integral_constant<int, SS + 1>{});
         static_for<2 * NB>([&](auto ab) {
           constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
-          acc[A][N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[A][s], kf[N], acc[A][N], 0, 0, 0);
+          acc[A][N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[A][SS], kf[SS & 1][N], acc[A][N], 0, 0, 0);
         });
       });
       const bool full = (!causal || c0 + KB - 1 <= r0) && (r0 + 63 < T) && (c0 + KB - 1 < T);
@@ -145,9 +166,15 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         });
       }
     }
-    if (more) sstore(cur ^ 1);
+    if (more) sstore(cur ^ 1, std::integral_constant<int, SS>{});
     barrier();
+  };
+  int kb = 0;
+  for (; kb + 1 < nkb; kb += 2) {
+    body(kb, S0{});
+    body(kb + 1, S1{});
   }
+  if (kb < nkb) body(kb, S0{});
 
   const int has_nan = __any(m != m) ? 1 : 0;
   m = wave_max(m);
