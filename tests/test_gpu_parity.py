@@ -4,7 +4,8 @@ identical seeded inputs.
 Tolerances (stated per stage, on identical inputs):
   * Newton-Schulz output: relative Frobenius error <= 2e-2 per matrix
     (bf16 MFMA operands, fp32 accumulation; CPU emulation of the same
-    rounding points sits at 0.9-1.2e-2).
+    rounding points sits at 0.9-1.5e-2); degenerate and thin shapes follow
+    ns_tolerance (5e-2 below 8 rows, 3e-2 for 8-47 rows with n >= 8 m).
   * momentum (fp32): relative Frobenius error <= 1e-5; X0 = bf16(U): every
     element a faithful bf16 rounding of U within the fp32 error bound of its
     two fused multiply-adds; 1/||U||: rel <= 1e-5.
@@ -61,8 +62,17 @@ def ns_tolerance(rows, cols):
     bf16 rounding of its 1x1 / 2x2 Gram and polynomial matrices moves the
     single trajectory sigma -> p(sigma) directly, and |p'| ~ 1.1-1.3 along it
     over five steps; a CPU emulation of the same rounding points reaches
-    2.0-2.8e-2 on such inputs.  Those degenerate shapes are held to 5e-2."""
-    return 2e-2 if min(rows, cols) >= 8 else 5e-2
+    2.0-2.8e-2 on such inputs.  Those degenerate shapes are held to 5e-2.
+    Thin matrices with 8 <= min(rows, cols) < 48 and a long other side (e.g.
+    33 x 777, singular values within a factor 1.5 of each other) emulate at
+    1.4-2.4e-2 and are held to 3e-2; from 48 rows on the emulation stays
+    below 1.9e-2."""
+    m, n = min(rows, cols), max(rows, cols)
+    if m < 8:
+        return 5e-2
+    if m < 48 and n >= 8 * m:
+        return 3e-2
+    return 2e-2
 
 
 NS_SHAPES = [(96, 160), (200, 72), (128, 128), (1, 37), (37, 1), (300, 600), (640, 520), (520, 1100),
@@ -173,7 +183,7 @@ def check_step(mm, wl, host, devg, ws, hp, sample=None):
             assert em <= 1e-5
             assert x0_ulp <= 0
             assert einv <= 1e-5
-            assert eo <= 2e-2
+            assert eo <= ns_tolerance(grp.rows, grp.cols)
             assert wok
 
 
@@ -190,6 +200,49 @@ def test_muon_step_stages_ragged(mm, dev, dtype, ns_steps):
     ws = mm.muon_step(devg, hp)
     torch.cuda.synchronize()
     check_step(mm, wl, host, devg, ws, hp)
+
+
+def test_muon_step_sixteen_groups(mm, dev):
+    """The largest call the boundary accepts: MUON_MAX_GROUPS groups of
+    assorted ragged shapes (tall, wide, square, a single row or column, both
+    tile sizes) in one muon_step."""
+    import torch
+    say(f"[step] {mm.MAX_GROUPS} groups in one call")
+    g = gen.rng(99)
+    shapes = [(1, 37), (37, 1), (64, 64), (130, 70), (70, 130), (200, 200), (256, 100), (100, 256),
+              (300, 17), (17, 300), (520, 64), (64, 520), (96, 160), (512, 513), (513, 512), (33, 777)]
+    assert len(shapes) == mm.MAX_GROUPS
+    wl = gen.small_workload(tuple(shapes), batch=2, dtype="bf16")
+    host, devg = make_groups(wl, 13, dev)
+    hp = mm.HParams()
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    check_step(mm, wl, host, devg, ws, hp)
+
+
+def test_muon_step_strided_batches(mm, dev):
+    """Matrices batch_stride > rows * cols apart (views into a padded
+    buffer): the result matches the oracle and the gaps stay untouched."""
+    import torch
+    say("[step] strided batches")
+    wl = gen.small_workload(((150, 90), (90, 260)), batch=3, dtype="bf16")
+    host, dense = make_groups(wl, 14, dev)
+    devg, bigs = [], []
+    for (W, G, M), grp in zip(dense, wl.groups):
+        views = []
+        for t in (W, G, M):
+            big = torch.full((grp.batch, grp.rows + 5, grp.cols), 7.0, dtype=t.dtype, device=dev)
+            v = big[:, :grp.rows, :]
+            v.copy_(t)
+            views.append(v)
+            bigs.append(big)
+        devg.append(tuple(views))
+    hp = mm.HParams()
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    check_step(mm, wl, host, devg, ws, hp)
+    for big, grp in zip(bigs, [g for g in wl.groups for _ in range(3)]):
+        assert torch.all(big[:, grp.rows:, :] == 7.0), "a gap between matrices was written"
 
 
 def test_muon_step_no_nesterov_and_scales(mm, dev):
