@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the readings of the 24-layer decoder and the MoE stack")
     ap.add_argument("--seed", type=int, default=5000)
     ap.add_argument("--blas-reference", action="store_true",
                     help="time torch.matmul (hipBLASLt) on the full, unsymmetric Newton-Schulz "
@@ -234,7 +236,12 @@ def main():
     out["companion"] = companion(mm, torch, dev, seed, n_mats * m * n)
     out["companion"]["attn_fwd"] = attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, prof["qk_rowmax"])
     del Q, K, Wqkv, Wo, Gqkv, Go, Mqkv, Mo, ws, groups
-    out["layer_hidden2048"] = layer_hidden2048(mm, torch, dev, seed, args.steps, args.warmup)
+    torch.cuda.empty_cache()
+    out["layer_hidden2048"] = config_reading(mm, torch, dev, seed, 2, args.steps, args.warmup)
+    if not args.no_other_configs:
+        k = max(2, min(3, args.steps))
+        out["other_configs"] = {"dense_decoder_24_layers": config_reading(mm, torch, dev, seed, 3, k, 1),
+                                "moe_64_experts": config_reading(mm, torch, dev, seed, 4, k, 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
     print(json.dumps(out), flush=True)
@@ -271,19 +278,25 @@ def blas_reference(torch, reps=10):
     return res
 
 
-def layer_hidden2048(mm, torch, dev, seed, steps, warmup):
-    """The Muon step alone (no QK-Clip) on one transformer layer of hidden
-    2048: W_q, W_k, W_v, W_o 2048x2048, MLP up/gate 8192x2048, down 2048x8192,
-    bf16 params and low-rank-plus-noise grads, fp32 momentum.  A second
-    reading of the same metric; the headline line is the MuonClip layer,
-    whose step is the only one that covers every stage of the path."""
+def config_reading(mm, torch, dev, seed, idx, steps, warmup):
+    """The Muon step alone (no QK-Clip) on one of the other configurations,
+    drawn on the GPU with its recipe (bf16 params and grads, fp32 momentum;
+    grads N(0,1), low-rank-plus-noise, or low-rank-plus-noise with Zipf(1.1)
+    expert magnitudes).  A second reading of the same metric beside the
+    headline MuonClip layer, whose step is the only one that covers every
+    stage of the path."""
     from synthetic import generators as gen
-    wl = gen.workload(2)
+    wl = gen.workload(idx)
     groups = []
     for gi, gr in enumerate(wl.groups):
         W = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.02, seed + 100 + gi, dev, torch.bfloat16)
-        G = torch.stack([gen.lowrank_torch(gr.rows, gr.cols, seed + 200 + 10 * gi + b, dev)
-                         for b in range(gr.batch)])
+        if wl.grad_kind == "normal":
+            G = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 1.0, seed + 200 + gi, dev, torch.bfloat16)
+        else:
+            mags = gen.zipf_magnitudes(gen.rng(seed + 7), gr.batch) if wl.grad_kind == "lowrank_zipf" \
+                else [1.0] * gr.batch
+            G = torch.stack([gen.lowrank_torch(gr.rows, gr.cols, seed + 200 + 1000 * gi + b, dev,
+                                               magnitude=float(mags[b])) for b in range(gr.batch)])
         M = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.5, seed + 300 + gi, dev, torch.float32)
         groups.append((W, G, M))
     hp = mm.HParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=True,
@@ -305,11 +318,14 @@ def layer_hidden2048(mm, torch, dev, seed, steps, warmup):
         m, n = min(gr.rows, gr.cols), max(gr.rows, gr.cols)
         flop += gr.batch * wl.ns_steps * sum(ns_flops(m, n).values())
     ns_ms = sum(prof[k][0] for k in ("ns_syrk_xxt", "ns_syrk_poly", "ns_gemm_bx")) / steps
-    return {"workload": "one layer, hidden 2048: 4 x 2048x2048, 2 x 8192x2048, 1 x 2048x8192",
-            "steps_per_s": round(steps / el, 2), "ms_per_step": round(1e3 * el / steps, 3),
-            "ns_tflops": round(flop / (ns_ms * 1e-3) / 1e12, 1),
-            "ns_frac_mfma_peak": round(flop / (ns_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "kernels_ms_per_step": {k: round(v[0] / steps, 4) for k, v in prof.items() if v[1]}}
+    res = {"workload": wl.name + ": " + ", ".join(f"{g.batch} x {g.rows}x{g.cols}" for g in wl.groups),
+           "steps": steps, "steps_per_s": round(steps / el, 3), "ms_per_step": round(1e3 * el / steps, 3),
+           "ns_tflops": round(flop / (ns_ms * 1e-3) / 1e12, 1),
+           "ns_frac_mfma_peak": round(flop / (ns_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "kernels_ms_per_step": {k: round(v[0] / steps, 4) for k, v in prof.items() if v[1]}}
+    del groups, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, rowmax_prof, reps=5):
