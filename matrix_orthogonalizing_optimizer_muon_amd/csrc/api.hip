@@ -226,6 +226,19 @@ struct FinalOut {
 
 enum Stage { STAGE_SYRK = 0, STAGE_POLY = 1, STAGE_BX = 2 };
 
+// Compute units of the current device (one GEMM block runs per CU at a time);
+// 0 if the query fails, which turns the last-wave split off.
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b, float c, void* ws,
                    const FinalOut* fin) {
   GemmProb q{};
@@ -289,6 +302,7 @@ GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b,
 int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c, void* ws,
            const std::vector<FinalOut>* fins, hipStream_t s) {
   static const int kinds[3] = {KIND_NS_SYRK, KIND_NS_POLY, KIND_NS_BX};
+  static const int slice_kinds[3] = {KIND_NS_SYRK_SLICES, KIND_NS_POLY_SLICES, KIND_NS_BX};
   for (int t = 0; t < steps; ++t) {
     for (int stage = 0; stage < 3; ++stage) {
       if (stage == STAGE_POLY && c == 0.0f) continue;
@@ -309,7 +323,17 @@ int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c,
         L.band = (stage == STAGE_BX) ? 1 : 0;
         for (int k = 0; k < L.nprob; ++k)
           if (L.p[k].tn % 8 != 0) L.band = 0;
-        MUON_LAUNCH(kinds[stage], s, launch_ns_gemm(L, tile, stage, tiles, s));
+        // A symmetric 256-tile product whose tiles leave a last wave at most
+        // half full runs those last tiles as column halves in a second launch:
+        // the last wave then takes about half as long.
+        const int ncu = cu_count();
+        const int tail = (ncu > 0 && tiles > ncu) ? tiles % ncu : 0;
+        const bool split = (stage != STAGE_BX) && tile == 256 && tail > 0 && 2 * tail <= ncu;
+        MUON_LAUNCH(kinds[stage], s, launch_ns_gemm(L, tile, stage, split ? tiles - tail : tiles, s));
+        if (split) {
+          L.lin0 = tiles - tail;
+          MUON_LAUNCH(slice_kinds[stage], s, launch_ns_gemm_slices(L, stage, 2 * tail, s));
+        }
       }
     }
   }
@@ -629,7 +653,8 @@ int muon_profile_collect(double* total_ms, int64_t* launches, int n_kinds) {
 const char* muon_kernel_kind_name(int kind) {
   static const char* names[KIND_COUNT] = {"momentum_norm", "norm_finalize", "ns_syrk_xxt", "ns_syrk_poly",
                                           "ns_gemm_bx",    "param_update",  "qk_rowmax",   "qk_reduce",
-                                          "qk_rescale",    "adamw",         "attn_fwd"};
+                                          "qk_rescale",    "adamw",         "attn_fwd",
+                                          "ns_syrk_xxt_slices", "ns_syrk_poly_slices"};
   if (kind < 0 || kind >= KIND_COUNT) return "unknown";
   return names[kind];
 }

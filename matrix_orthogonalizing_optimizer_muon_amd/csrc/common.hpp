@@ -68,7 +68,9 @@ enum KernelKind {
   KIND_QK_RESCALE = 8,
   KIND_ADAMW = 9,
   KIND_ATTN_FWD = 10,
-  KIND_COUNT = 11
+  KIND_NS_SYRK_SLICES = 11,
+  KIND_NS_POLY_SLICES = 12,
+  KIND_COUNT = 13
 };
 
 // ---------------------------------------------------------------------------
@@ -103,6 +105,7 @@ struct GemmProb {
 struct GemmLaunch {
   int nprob;
   int band;         // non-symmetric products with tn % 8 == 0: column bands per XCD
+  int lin0;         // column-slice launches: first tile (in the launch's tile order) covered
   int prefix[kMaxProbs + 1];
   GemmProb p[kMaxProbs];
 };
@@ -164,6 +167,7 @@ struct UpdateLaunch {
 hipError_t launch_momentum_norm(const MomentumLaunch& L, int grad_dtype, int nblocks, hipStream_t s);
 hipError_t launch_norm_finalize(const FinalizeLaunch& L, int nmats, hipStream_t s);
 hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks, hipStream_t s);
+hipError_t launch_ns_gemm_slices(const GemmLaunch& L, int stage, int nblocks, hipStream_t s);
 hipError_t launch_param_update(const UpdateLaunch& L, int param_dtype, int64_t nblocks, hipStream_t s);
 hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int H, int d_head,
                             int causal, float* partial, int nqb, hipStream_t s);

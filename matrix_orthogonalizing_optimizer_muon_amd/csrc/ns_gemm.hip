@@ -15,9 +15,13 @@
 // tile twice (in place and mirrored).  X is kept in both layouts (X and X^T):
 // the epilogue of X' writes both, so no transpose pass is ever needed.
 //
-// Tiling: TILE x TILE output per 256-thread block, 2 x 2 waves, each wave a
-// (TILE/2) x (TILE/2) sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16),
-// K staged 32 at a time in double-buffered, padded LDS.
+// Tiling: TILE x TILE output per 512-thread block, 2 x 4 waves, each wave a
+// (TILE/2) x (TILE/4) sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16),
+// K staged 64 at a time in double-buffered, padded LDS.  When a symmetric
+// product's tile count leaves a partial last wave on the chip, those last
+// tiles run instead as 256 x 128 column halves (4 x 2 waves of 64 x 64) in a
+// second launch: twice the blocks at half the work each, with every output
+// element accumulated over K in the same order as in a whole tile.
 #include <utility>
 
 #include "common.hpp"
@@ -63,13 +67,14 @@ __device__ __forceinline__ u32x2_t epi_quad(const f32x16_t& acc, const EpiArgs& 
   return __builtin_bit_cast(u32x2_t, __builtin_convertvector(v, bf16x4_t));
 }
 
-// Stage the TILE x TILE tile src[r0 + r][c0 + c] (leading dimension ld) in
-// LDS with row pitch EP.  The caller guarantees the whole tile lies inside
+// Stage the ROWS x COLS block src[r0 + r][c0 + c] (leading dimension ld) in
+// LDS with row pitch EP.  The caller guarantees the whole block lies inside
 // src (the epilogue's E operand is always a padded workspace matrix).
-template <int TILE, int EP, int NT>
+template <int ROWS, int COLS, int EP, int NT>
 __device__ __forceinline__ void copy_in(bf16_t* st, const bf16_t* src, int ld, int r0, int c0, int tid) {
-  constexpr int CPRW = TILE / 8;
-  constexpr int N = TILE * CPRW / NT;
+  constexpr int CPRW = COLS / 8;
+  constexpr int N = ROWS * CPRW / NT;
+  static_assert(ROWS * CPRW % NT == 0, "copy map must cover the block exactly");
   static_for<N>([&](auto k) {
     const int c = tid + NT * decltype(k)::value;
     const int row = c / CPRW, cc = (c % CPRW) * 8;
@@ -78,14 +83,15 @@ __device__ __forceinline__ void copy_in(bf16_t* st, const bf16_t* src, int ld, i
   });
 }
 
-// Copy a TILE x TILE bf16 tile staged in LDS (row pitch EP elements) to
+// Copy a ROWS x COLS bf16 block staged in LDS (row pitch EP elements) to
 // dst[r][c] (leading dimension ld), rows < rvalid - r0, cols < cvalid - c0,
 // 16 bytes per store where the chunk is whole and aligned.
-template <int TILE, int EP, int NT>
+template <int ROWS, int COLS, int EP, int NT>
 __device__ __forceinline__ void copy_out(const bf16_t* st, bf16_t* dst, int ld, int r0, int c0, int rvalid,
                                          int cvalid, bool vec16, int tid) {
-  constexpr int CPRW = TILE / 8;
-  constexpr int N = TILE * CPRW / NT;
+  constexpr int CPRW = COLS / 8;
+  constexpr int N = ROWS * CPRW / NT;
+  static_assert(ROWS * CPRW % NT == 0, "copy map must cover the block exactly");
 #pragma unroll 4
   for (int k = 0; k < N; ++k) {
     const int c = tid + NT * k;
@@ -103,26 +109,44 @@ __device__ __forceinline__ void copy_out(const bf16_t* st, bf16_t* dst, int ld, 
   }
 }
 
-template <int TILE, int STAGE>
+// One block computes a TM x TN output tile of a product whose tiles are
+// TM x TM (TN = TM), or one of the TM / TN column slices of such a tile
+// (TN < TM: the slices of the last, partial wave of a launch).  Eight waves in
+// a WR x WC grid.
+template <int TM, int TN, int STAGE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gemm_kernel(GemmLaunch L) {
   constexpr int NT = 512;
-  constexpr int WT = TILE / 2;       // wave sub-tile rows
-  constexpr int WN = TILE / 4;       // wave sub-tile cols
-  constexpr int F = WT / 32;         // 32x32 MFMA blocks along rows
-  constexpr int G = WN / 32;         // along cols
-  constexpr int CPR = kBK / 8;        // 16-byte chunks per tile row of a K slice
-  constexpr int RPP = NT / CPR;       // tile rows covered by one pass of the block
-  constexpr int NCH = TILE / RPP;     // passes (chunks per thread per operand)
-  static_assert(TILE % RPP == 0, "staging map must cover the tile exactly");
+  constexpr int WC = (TN == TM) ? 4 : 2;   // waves along the tile's columns
+  constexpr int WR = 8 / WC;               // and rows
+  constexpr int WT = TM / WR;              // wave sub-tile rows
+  constexpr int WN = TN / WC;              // wave sub-tile cols
+  constexpr int F = WT / 32;               // 32x32 MFMA blocks along rows
+  constexpr int G = WN / 32;               // along cols
+  constexpr int NSLICE = TM / TN;          // column slices per tile
+  constexpr int CPR = kBK / 8;             // 16-byte chunks per tile row of a K slice
+  constexpr int RPP = NT / CPR;            // tile rows covered by one pass of the block
+  constexpr int NCP = TM / RPP;            // passes (chunks per thread) for P
+  constexpr int NCQ = TN / RPP;            // and for Q
+  static_assert(TM % RPP == 0 && TN % RPP == 0, "staging map must cover the tile exactly");
+  static_assert(F >= 1 && G >= 1 && TM % TN == 0, "wave grid must fit the tile");
 
   // two stages of the P and Q slices; the epilogue reuses the whole buffer
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * TILE * kPitch];
-  auto sP = [&](int buf) { return smem + buf * TILE * kPitch; };
-  auto sQ = [&](int buf) { return smem + (2 + buf) * TILE * kPitch; };
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (TM + TN) * kPitch];
+  auto sP = [&](int buf) { return smem + buf * TM * kPitch; };
+  auto sQ = [&](int buf) { return smem + 2 * TM * kPitch + buf * TN * kPitch; };
 
-  // ---- block -> (problem, matrix, tile)
-  const int lin = L.band ? static_cast<int>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+  // ---- block -> (problem, matrix, tile, column slice)
+  int lin, slice = 0;
+  if (NSLICE == 1) {
+    lin = L.band ? static_cast<int>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+  } else {
+    // the slices of one tile are adjacent in each XCD's contiguous range, so
+    // they mostly share that XCD's cache for the common P panel
+    const int r = xcd_remap(blockIdx.x, gridDim.x);
+    lin = L.lin0 + r / NSLICE;
+    slice = r % NSLICE;
+  }
   int gi = 0;
   while (gi + 1 < L.nprob && lin >= L.prefix[gi + 1]) ++gi;
   const GemmProb& p = L.p[gi];
@@ -185,15 +209,17 @@ void ns_gemm_kernel(GemmLaunch L) {
     ti = first + r % gm;
     tj = r / gm;
   }
+  const int row0 = ti * TM;                 // first output row of this block
+  const int col0 = tj * TM + slice * TN;    // first output column
 
-  const bf16_t* Pg = p.P + mat * p.sP + static_cast<int64_t>(ti) * TILE * p.ldp;
-  const bf16_t* Qg = p.Q + mat * p.sQ + static_cast<int64_t>(tj) * TILE * p.ldq;
+  const bf16_t* Pg = p.P + mat * p.sP + static_cast<int64_t>(row0) * p.ldp;
+  const bf16_t* Qg = p.Q + mat * p.sQ + static_cast<int64_t>(col0) * p.ldq;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr0 = (wave >> 2) * WT;  // wave row offset in the tile
-  const int wc0 = (wave & 3) * WN;   // wave col offset in the tile
+  const int wr0 = (wave / WC) * WT;  // wave row offset in the tile
+  const int wc0 = (wave % WC) * WN;  // wave col offset in the tile
 
   // global -> register staging map: chunk c of this thread covers tile row
   // (tid / CPR + RPP * c), 8 bf16 at column 8 * (tid % CPR) of the K slice.
@@ -208,22 +234,18 @@ void ns_gemm_kernel(GemmLaunch L) {
   const int vQ = (lrow * p.ldq + lkc) * 2;
   const int sstrP = RPP * p.ldp * 2, sstrQ = RPP * p.ldq * 2;
   const int sOff = (lrow * kPitch + lkc) * 2;   // bytes inside an LDS stage
-  u32x4_t rP[NCH], rQ[NCH];
+  u32x4_t rP[NCP], rQ[NCQ];
   const int KT = p.K / kBK;
   auto gload = [&](int kslice) {
     const int kb = min(kslice, KT - 1) * kBK * 2;
-    static_for<NCH>([&](auto c) {
-      rP[c] = __builtin_amdgcn_raw_buffer_load_b128(rsP, vP, kb + c * sstrP, 0);
-      rQ[c] = __builtin_amdgcn_raw_buffer_load_b128(rsQ, vQ, kb + c * sstrQ, 0);
-    });
+    static_for<NCP>([&](auto c) { rP[c] = __builtin_amdgcn_raw_buffer_load_b128(rsP, vP, kb + c * sstrP, 0); });
+    static_for<NCQ>([&](auto c) { rQ[c] = __builtin_amdgcn_raw_buffer_load_b128(rsQ, vQ, kb + c * sstrQ, 0); });
   };
   auto sstore = [&](int buf) {
     char* bP = reinterpret_cast<char*>(sP(buf)) + sOff;
     char* bQ = reinterpret_cast<char*>(sQ(buf)) + sOff;
-    static_for<NCH>([&](auto c) {
-      *reinterpret_cast<u32x4_t*>(bP + c * RPP * kPitch * 2) = rP[c];
-      *reinterpret_cast<u32x4_t*>(bQ + c * RPP * kPitch * 2) = rQ[c];
-    });
+    static_for<NCP>([&](auto c) { *reinterpret_cast<u32x4_t*>(bP + c * RPP * kPitch * 2) = rP[c]; });
+    static_for<NCQ>([&](auto c) { *reinterpret_cast<u32x4_t*>(bQ + c * RPP * kPitch * 2) = rQ[c]; });
   };
   // barrier without the workgroup fence of __syncthreads (that fence would
   // drain the prefetch loads): this wave's LDS traffic done, then s_barrier
@@ -252,7 +274,7 @@ void ns_gemm_kernel(GemmLaunch L) {
       acc[A][B] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][A], fb[slot][B], acc[A][B], 0, 0, 0);
     });
   };
-  // interleave: per MFMA one LDS read (first 2F MFMAs), optionally global loads
+  // interleave: per MFMA one LDS read (first F+G MFMAs), optionally global loads
   auto pattern = [&](int nv, int nw) {
     for (int q = 0; q < F * G; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -279,7 +301,7 @@ void ns_gemm_kernel(GemmLaunch L) {
         gload(kt + 2);
       }
       mfmas(std::integral_constant<int, SS & 1>{});
-      pattern(SS == S - 2 ? 2 * NCH : 0, SS == S - 2 ? 2 * NCH : 0);
+      pattern(SS == S - 2 ? NCP + NCQ : 0, SS == S - 2 ? NCP + NCQ : 0);
     });
     barrier();
     read_frags(cur ^ 1, 0, std::integral_constant<int, 0>{});
@@ -289,8 +311,8 @@ void ns_gemm_kernel(GemmLaunch L) {
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue.  Element e of acc[a][b] holds C[i][j] with
-  //   i = tile_i0 + wr0 + 32 a + 8 (e / 4) + 4 (lane / 32) + (e % 4),
-  //   j = tile_j0 + wc0 + 32 b + (lane % 32).
+  //   i = row0 + wr0 + 32 a + 8 (e / 4) + 4 (lane / 32) + (e % 4),
+  //   j = col0 + wc0 + 32 b + (lane % 32).
   // The rounded tile goes through LDS so both layouts leave in 16-byte
   // stores of whole rows (direct stores from this layout would be 2- or
   // 8-byte pieces of many cache lines).
@@ -299,16 +321,18 @@ void ns_gemm_kernel(GemmLaunch L) {
     const float al = p.alpha[mat];
     sc = (p.alpha_pow == 2) ? al * al : al;
   }
-  constexpr int EP = TILE + 8;                 // staged tile row pitch (bf16)
-  static_assert(TILE * EP <= 4 * TILE * kPitch, "staged tile must fit the LDS buffer");
+  constexpr int EPC = TN + 8;                  // staged C tile row pitch (bf16), TM rows
+  constexpr int EPT = TM + 8;                  // staged Ct / Et tile row pitch, TN rows
+  static_assert(TM * EPC <= 2 * (TM + TN) * kPitch && TN * EPT <= 2 * (TM + TN) * kPitch,
+                "staged tile must fit the LDS buffer");
   EpiArgs e;
   e.ca = p.c_acc * sc;
   e.ce = p.c_e * sc;
   e.cd = p.c_diag * sc;
   e.Et = nullptr;
-  e.lde = EP;
-  e.gi0 = ti * TILE + wr0 + 4 * (lane >> 5);
-  e.gj0 = tj * TILE + wc0 + (lane & 31);
+  e.lde = EPT;
+  e.gi0 = row0 + wr0 + 4 * (lane >> 5);
+  e.gj0 = col0 + wc0 + (lane & 31);
   e.li0 = wr0 + 4 * (lane >> 5);
   e.lj0 = wc0 + (lane & 31);
   bf16_t* C = p.C ? p.C + mat * p.sC : nullptr;
@@ -316,8 +340,8 @@ void ns_gemm_kernel(GemmLaunch L) {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();                // every wave is done with the K slices
   if (p.Et) {
-    // E[j][i] tile (the transposed layout of this output tile), coalesced into LDS
-    copy_in<TILE, EP, NT>(smem, p.Et + mat * p.sEt, p.lde, tj * TILE, ti * TILE, tid);
+    // E[j][i] block (the transposed layout of this output block), coalesced into LDS
+    copy_in<TN, TM, EPT, NT>(smem, p.Et + mat * p.sEt, p.lde, col0, row0, tid);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     e.Et = smem;
@@ -339,11 +363,11 @@ void ns_gemm_kernel(GemmLaunch L) {
     static_for<F * G * 4>([&](auto x) {
       constexpr int X = decltype(x)::value;
       constexpr int A = X / (4 * G), B = (X / 4) % G, Qd = X % 4;
-      *reinterpret_cast<u32x2_t*>(smem + (lj0 + 32 * B) * EP + li0 + 32 * A + 8 * Qd) = quad[A][B][Qd];
+      *reinterpret_cast<u32x2_t*>(smem + (lj0 + 32 * B) * EPT + li0 + 32 * A + 8 * Qd) = quad[A][B][Qd];
     });
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
-    copy_out<TILE, EP, NT>(smem, Ct, p.ldct, tj * TILE, ti * TILE, p.nvalid, p.mvalid, p.ct16 != 0, tid);
+    copy_out<TN, TM, EPT, NT>(smem, Ct, p.ldct, col0, row0, p.nvalid, p.mvalid, p.ct16 != 0, tid);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
   }
@@ -352,16 +376,16 @@ void ns_gemm_kernel(GemmLaunch L) {
     static_for<F * G * 4>([&](auto x) {
       constexpr int X = decltype(x)::value;
       constexpr int A = X / (4 * G), B = (X / 4) % G, Qd = X % 4;
-      bf16_t* d = smem + (li0 + 32 * A + 8 * Qd) * EP + lj0 + 32 * B;
+      bf16_t* d = smem + (li0 + 32 * A + 8 * Qd) * EPC + lj0 + 32 * B;
       const u32x2_t w = quad[A][B][Qd];
       d[0] = static_cast<bf16_t>(w[0] & 0xffff);
-      d[EP] = static_cast<bf16_t>(w[0] >> 16);
-      d[2 * EP] = static_cast<bf16_t>(w[1] & 0xffff);
-      d[3 * EP] = static_cast<bf16_t>(w[1] >> 16);
+      d[EPC] = static_cast<bf16_t>(w[0] >> 16);
+      d[2 * EPC] = static_cast<bf16_t>(w[1] & 0xffff);
+      d[3 * EPC] = static_cast<bf16_t>(w[1] >> 16);
     });
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
-    copy_out<TILE, EP, NT>(smem, C, p.ldc, ti * TILE, tj * TILE, p.mvalid, p.nvalid, p.c16 != 0, tid);
+    copy_out<TM, TN, EPC, NT>(smem, C, p.ldc, row0, col0, p.mvalid, p.nvalid, p.c16 != 0, tid);
   }
 }
 
@@ -371,14 +395,24 @@ hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks,
   // one symbol per (tile, stage) so kernel traces attribute time per product
   const dim3 grid(nblocks), block(512);
   if (tile == 256) {
-    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<256, 0>), grid, block, 0, s, L);
-    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<256, 1>), grid, block, 0, s, L);
-    else hipLaunchKernelGGL((ns_gemm_kernel<256, 2>), grid, block, 0, s, L);
+    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<256, 256, 0>), grid, block, 0, s, L);
+    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<256, 256, 1>), grid, block, 0, s, L);
+    else hipLaunchKernelGGL((ns_gemm_kernel<256, 256, 2>), grid, block, 0, s, L);
   } else {
-    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<128, 0>), grid, block, 0, s, L);
-    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<128, 1>), grid, block, 0, s, L);
-    else hipLaunchKernelGGL((ns_gemm_kernel<128, 2>), grid, block, 0, s, L);
+    if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<128, 128, 0>), grid, block, 0, s, L);
+    else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<128, 128, 1>), grid, block, 0, s, L);
+    else hipLaunchKernelGGL((ns_gemm_kernel<128, 128, 2>), grid, block, 0, s, L);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_gemm_slices(const GemmLaunch& L, int stage, int nblocks, hipStream_t s) {
+  // 256 x 128 column slices of 256-tiles: blocks 2u and 2u + 1 (after the XCD
+  // remap) are the two halves of tile L.lin0 + u
+  const dim3 grid(nblocks), block(512);
+  if (stage == 0) hipLaunchKernelGGL((ns_gemm_kernel<256, 128, 0>), grid, block, 0, s, L);
+  else if (stage == 1) hipLaunchKernelGGL((ns_gemm_kernel<256, 128, 1>), grid, block, 0, s, L);
+  else hipLaunchKernelGGL((ns_gemm_kernel<256, 128, 2>), grid, block, 0, s, L);
   return hipGetLastError();
 }
 

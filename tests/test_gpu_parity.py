@@ -100,6 +100,45 @@ def test_ns_orthogonalize_matches_oracle(mm, dev, shape, dtype):
         assert err <= ns_tolerance(r, c)
 
 
+# Batches whose symmetric products (X X^T and the polynomial) leave a last
+# wave at most half full on the chip: those last 256-tiles run as 256 x 128
+# column halves in a second launch.
+SLICE_CASES = [(120, 512, 512), (50, 640, 1300)]
+
+
+@pytest.mark.parametrize("batch,r,c", SLICE_CASES)
+def test_ns_last_wave_slices(mm, dev, batch, r, c):
+    """Matrices whose tiles fall in the column-half launch match the oracle,
+    and agree bit for bit with the same matrix orthogonalised alone (a launch
+    too small to split): every output element accumulates over K in the same
+    order in a half tile as in a whole one."""
+    import torch
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    T = -(-min(r, c) // 256)
+    per = T * (T + 1) // 2
+    tiles = batch * per
+    tail = tiles % ncu
+    say(f"[ns slices] batch={batch} shape=({r}, {c}): {tiles} symmetric tiles on {ncu} CUs, last wave {tail}")
+    if not (tiles > ncu and 0 < tail <= ncu // 2):
+        pytest.skip(f"no half-full last wave with {ncu} compute units")
+    first = (tiles - tail) // per          # first matrix with a tile in the half-tile launch
+    g = gen.rng(batch * 7 + r)
+    X = gen.gaussian(g, (batch, r, c), 1.0).astype(np.float32)
+    xd = to_dev(X, dev)
+    got = to_host(mm.ns_orthogonalize(xd))
+    torch.cuda.synchronize()
+    for b in sorted({0, first, (first + batch) // 2, batch - 1}):
+        alone = to_host(mm.ns_orthogonalize(xd[b:b + 1].contiguous()))[0]
+        torch.cuda.synchronize()
+        say(f"   matrix {b}: {'in' if b >= first else 'before'} the half-tile launch; "
+            f"differing elements vs alone {int(np.count_nonzero(alone != got[b]))}")
+        assert np.array_equal(alone, got[b])
+    for b in (first, batch - 1):
+        err = rel_fro(O.bf16_bits_to_f64(got[b]), O.newton_schulz(X[b].astype(np.float64)))
+        say(f"   matrix {b}: rel err vs oracle {err:.3e}")
+        assert err <= ns_tolerance(r, c)
+
+
 # ---------------------------------------------------------------------------
 # one Muon step, stage by stage
 # ---------------------------------------------------------------------------
