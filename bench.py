@@ -241,6 +241,7 @@ def main():
     del Q, K, Wqkv, Wo, Gqkv, Go, Mqkv, Mo, ws, groups
     torch.cuda.empty_cache()
     out["layer_hidden2048"] = config_reading(mm, torch, dev, seed, 2, args.steps, args.warmup)
+    out["single_matrix_256x128"] = small_matrix_reading(mm, torch, dev, seed)
     if not args.no_other_configs:
         k = max(2, min(3, args.steps))
         out["other_configs"] = {"dense_decoder_24_layers": config_reading(mm, torch, dev, seed, 3, k, 1),
@@ -279,6 +280,52 @@ def blas_reference(torch, reps=10):
         res[name] = {"ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 1)}
     res["ns_iteration_ms"] = round(sum(v["ms"] for k, v in res.items() if isinstance(v, dict)), 3)
     return res
+
+
+def small_matrix_reading(mm, torch, dev, seed, steps=200, warmup=20):
+    """The single fp32 256x128 matrix: 10 fresh N(0,1) gradients drawn on the
+    device beforehand and cycled, W ~ N(0, 0.02^2), momentum from zero,
+    Nesterov, 5 Newton-Schulz steps.  Latency-bound: one launch per step (the
+    whole step in one workgroup); reported as microseconds per step, eagerly
+    and replayed from a captured HIP graph."""
+    from synthetic import generators as gen
+    wl = gen.workload(1)
+    gr = wl.groups[0]
+    W = gen.bulk_normal_torch((gr.rows, gr.cols), wl.weight_std, seed + 500, dev, torch.float32)
+    M = torch.zeros((gr.rows, gr.cols), dtype=torch.float32, device=dev)
+    grads = [gen.bulk_normal_torch((gr.rows, gr.cols), 1.0, seed + 510 + k, dev, torch.float32)
+             for k in range(10)]
+    hp = mm.HParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=True,
+                    ns_steps=wl.ns_steps, ns_coeffs=wl.ns_coeffs, ns_eps=wl.ns_eps, rms_target=wl.rms_target)
+    ws = torch.empty(mm.workspace_size([(W, grads[0], M)]), dtype=torch.uint8, device=dev)
+    for k in range(warmup):
+        mm.muon_step([(W, grads[k % 10], M)], hp, workspace=ws)
+    torch.cuda.synchronize()
+    mm.profile_enable(True)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        mm.muon_step([(W, grads[k % 10], M)], hp, workspace=ws)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    prof = mm.profile_collect()
+    mm.profile_enable(False)
+    # one captured step on a side stream, replayed (the gradient buffer is fixed)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        mm.muon_step([(W, grads[0], M)], hp, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    el_graph = time.perf_counter() - t0
+    return {"workload": "1 x 256x128 fp32, 5 Newton-Schulz steps", "steps": steps,
+            "us_per_step": round(1e6 * el / steps, 2), "steps_per_s": round(steps / el, 1),
+            "graph_us_per_step": round(1e6 * el_graph / steps, 2),
+            "kernels_us_per_step": {k: round(1e3 * v[0] / steps, 2) for k, v in prof.items() if v[1]},
+            "launches_per_step": sum(v[1] for v in prof.values()) / steps}
 
 
 def config_reading(mm, torch, dev, seed, idx, steps, warmup):

@@ -226,6 +226,11 @@ struct FinalOut {
 
 enum Stage { STAGE_SYRK = 0, STAGE_POLY = 1, STAGE_BX = 2 };
 
+// Groups whose wide view fits the single-workgroup step (X and A in LDS).
+bool small_ok(int rows, int cols) {
+  return std::min(rows, cols) <= kSmallMaxM && std::max(rows, cols) <= kSmallMaxN;
+}
+
 // Compute units of the current device (one GEMM block runs per CU at a time);
 // 0 if the query fails, which turns the last-wave split off.
 int cu_count() {
@@ -405,23 +410,78 @@ int muon_step(const muon_group_t* groups, int n_groups, int param_dtype, const m
   std::vector<Plan> plans = plans_for(groups, n_groups, need);
   if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
 
+  const int fin = hp->ns_steps & 1;
+  // small groups: the whole step in one launch, one workgroup per matrix,
+  // with X0, 1/||U|| and O left in the same workspace places as below
+  SmallLaunch S{};
+  int small_mats = 0;
+  std::vector<int> big;
+  for (int g = 0; g < n_groups; ++g) {
+    const Plan& p = plans[g];
+    if (!small_ok(p.rows, p.cols)) {
+      big.push_back(g);
+      continue;
+    }
+    SmallGroup& q = S.g[S.ngroups];
+    q.G = groups[g].grad;
+    q.M = groups[g].momentum;
+    q.W = groups[g].param;
+    q.bstride = p.bstride;
+    q.rows = p.rows;
+    q.cols = p.cols;
+    q.tall = p.tall ? 1 : 0;
+    q.m = p.m;
+    q.n = p.n;
+    q.X0 = at<bf16_t>(workspace, p.off_X[0]);
+    q.x0_stride = static_cast<int64_t>(p.mp) * p.np;
+    q.x0_ld = p.np;
+    q.O = at<bf16_t>(workspace, p.tall ? p.off_Xt[fin] : p.off_X[fin]);
+    q.o_stride = static_cast<int64_t>(p.mp) * p.np;
+    q.o_ld = p.tall ? p.mp : p.np;
+    q.inv = at<float>(workspace, p.off_inv);
+    const float scale = update_scale(hp->scale_mode, p.rows, p.cols, hp->rms_target);
+    q.decay = static_cast<float>(1.0 - static_cast<double>(hp->lr) * hp->weight_decay);
+    q.step = static_cast<float>(static_cast<double>(hp->lr) * scale);
+    q.vec = (p.cols % 8 == 0) && (p.bstride % 8 == 0) && aligned(q.G, 16) && aligned(q.M, 16) && aligned(q.W, 16);
+    q.ovec = (p.cols % 8 == 0) && aligned(q.O, 16);
+    S.prefix[S.ngroups] = small_mats;
+    small_mats += p.batch;
+    ++S.ngroups;
+  }
+  S.prefix[S.ngroups] = small_mats;
+  if (S.ngroups > 0) {
+    S.mu = hp->momentum;
+    S.nesterov = hp->nesterov ? 1 : 0;
+    S.eps = hp->ns_eps;
+    S.steps = hp->ns_steps;
+    S.a = hp->ns_a;
+    S.b = hp->ns_b;
+    S.c = hp->ns_c;
+    MUON_LAUNCH(KIND_SMALL_STEP, stream, launch_small_step(S, param_dtype, small_mats, stream));
+  }
+  if (big.empty()) return MUON_OK;
+
+  std::vector<Plan> bp;
   std::vector<PrepIn> ins;
-  for (int g = 0; g < n_groups; ++g) ins.push_back({groups[g].grad, groups[g].momentum});
-  st = launch_prep(plans, ins, param_dtype, hp->momentum, hp->nesterov ? 1 : 0, workspace, stream);
+  for (int g : big) {
+    bp.push_back(plans[g]);
+    ins.push_back({groups[g].grad, groups[g].momentum});
+  }
+  st = launch_prep(bp, ins, param_dtype, hp->momentum, hp->nesterov ? 1 : 0, workspace, stream);
   if (st != MUON_OK) return st;
-  st = launch_finalize(plans, hp->ns_eps, workspace, stream);
+  st = launch_finalize(bp, hp->ns_eps, workspace, stream);
   if (st != MUON_OK) return st;
-  st = run_ns(plans, hp->ns_steps, hp->ns_a, hp->ns_b, hp->ns_c, workspace, nullptr, stream);
+  st = run_ns(bp, hp->ns_steps, hp->ns_a, hp->ns_b, hp->ns_c, workspace, nullptr, stream);
   if (st != MUON_OK) return st;
 
   UpdateLaunch U{};
-  U.ngroups = n_groups;
+  U.ngroups = static_cast<int>(big.size());
   int64_t blocks = 0;
   const size_t esz = param_dtype == MUON_DTYPE_BF16 ? 2 : 4;
-  const int fin = hp->ns_steps & 1;
-  for (int g = 0; g < n_groups; ++g) {
-    const Plan& p = plans[g];
-    UpdateGroup& u = U.g[g];
+  for (int k = 0; k < U.ngroups; ++k) {
+    const int g = big[k];
+    const Plan& p = bp[k];
+    UpdateGroup& u = U.g[k];
     u.W = groups[g].param;
     u.O = at<bf16_t>(workspace, p.tall ? p.off_Xt[fin] : p.off_X[fin]);
     u.bstride = p.bstride;
@@ -436,10 +496,10 @@ int muon_step(const muon_group_t* groups, int n_groups, int param_dtype, const m
     const float scale = update_scale(hp->scale_mode, p.rows, p.cols, hp->rms_target);
     u.decay = static_cast<float>(1.0 - static_cast<double>(hp->lr) * hp->weight_decay);
     u.step = static_cast<float>(static_cast<double>(hp->lr) * scale);
-    U.prefix[g] = blocks;
+    U.prefix[k] = blocks;
     blocks += u.blocks;
   }
-  U.prefix[n_groups] = blocks;
+  U.prefix[U.ngroups] = blocks;
   MUON_LAUNCH(KIND_PARAM_UPDATE, stream, launch_param_update(U, param_dtype, blocks, stream));
   return MUON_OK;
 }
@@ -462,6 +522,34 @@ int ns_orthogonalize(const void* in, int in_dtype, uint16_t* out, int batch, int
   std::vector<Plan> plans;
   plans.push_back(make_plan(batch, rows, cols, batch_stride, need));
   if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
+  if (small_ok(rows, cols)) {
+    const Plan& p = plans[0];
+    SmallLaunch S{};
+    S.ngroups = 1;
+    S.prefix[0] = 0;
+    S.prefix[1] = batch;
+    SmallGroup& q = S.g[0];
+    q.G = in;
+    q.bstride = batch_stride;
+    q.rows = rows;
+    q.cols = cols;
+    q.tall = p.tall ? 1 : 0;
+    q.m = p.m;
+    q.n = p.n;
+    q.O = reinterpret_cast<bf16_t*>(out);
+    q.o_stride = static_cast<int64_t>(rows) * cols;
+    q.o_ld = cols;
+    q.inv = at<float>(workspace, p.off_inv);
+    q.vec = (cols % 8 == 0) && (batch_stride % 8 == 0) && aligned(in, 16);
+    q.ovec = (cols % 8 == 0) && aligned(out, 16);
+    S.eps = eps;
+    S.steps = steps;
+    S.a = a;
+    S.b = b;
+    S.c = c;
+    MUON_LAUNCH(KIND_SMALL_STEP, stream, launch_small_step(S, in_dtype, batch, stream));
+    return MUON_OK;
+  }
   std::vector<PrepIn> ins{{in, nullptr}};
   int st = launch_prep(plans, ins, in_dtype, 0.0f, 0, workspace, stream);
   if (st != MUON_OK) return st;
@@ -654,7 +742,7 @@ const char* muon_kernel_kind_name(int kind) {
   static const char* names[KIND_COUNT] = {"momentum_norm", "norm_finalize", "ns_syrk_xxt", "ns_syrk_poly",
                                           "ns_gemm_bx",    "param_update",  "qk_rowmax",   "qk_reduce",
                                           "qk_rescale",    "adamw",         "attn_fwd",
-                                          "ns_syrk_xxt_slices", "ns_syrk_poly_slices"};
+                                          "ns_syrk_xxt_slices", "ns_syrk_poly_slices", "small_step"};
   if (kind < 0 || kind >= KIND_COUNT) return "unknown";
   return names[kind];
 }

@@ -108,12 +108,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
       });
     });
   };
-  // barrier without the workgroup fence of __syncthreads (it would drain the
-  // prefetch loads): this wave's LDS traffic done, then s_barrier
-  auto barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-  };
+  // LDS-only barrier: the prefetch loads stay in flight across it
+  auto barrier = [&]() { lds_barrier(); };
 
   f32x16_t o[kD / 32];
   static_for<kD / 32>([&](auto i) { o[i] = f32x16_t{}; });

@@ -46,6 +46,16 @@ __device__ __forceinline__ void static_for(Fn&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Workgroup barrier ordering LDS accesses only: release / acquire fences
+// restricted to the local address space, so the wait before s_barrier
+// covers LDS operations and not global loads in flight (prefetches) or
+// global stores (which __syncthreads would wait for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
 // This bijection hands each XCD one contiguous range of logical work items,
 // so the blocks an XCD runs at the same time share operands in its L2.
@@ -70,7 +80,8 @@ enum KernelKind {
   KIND_ATTN_FWD = 10,
   KIND_NS_SYRK_SLICES = 11,
   KIND_NS_POLY_SLICES = 12,
-  KIND_COUNT = 13
+  KIND_SMALL_STEP = 13,
+  KIND_COUNT = 14
 };
 
 // ---------------------------------------------------------------------------
@@ -163,12 +174,50 @@ struct UpdateLaunch {
   UpdateGroup g[kMaxProbs];
 };
 
+// Whole step for small matrices (wide view m <= 128, n <= 256), one
+// workgroup per matrix: momentum and lookahead, Frobenius norm, the
+// Newton-Schulz iteration with every operand in LDS, and the update.
+constexpr int kSmallMaxM = 128;
+constexpr int kSmallMaxN = 256;
+
+struct SmallGroup {
+  const void* G;      // grad (param dtype) or the input of ns_orthogonalize, [rows][cols]
+  float* M;           // momentum (null: U = G)
+  void* W;            // param (null: no update)
+  int64_t bstride;    // elements between matrices of G / M / W
+  int rows, cols;     // original layout
+  int tall;           // rows > cols: the wide view is the transpose
+  int m, n;           // wide view, m <= n
+  bf16_t* X0;         // bf16(U), wide [m][n] with ld x0_ld, stride x0_stride (or null)
+  int64_t x0_stride;
+  int x0_ld;
+  bf16_t* O;          // the result in the original layout [rows][cols], ld o_ld
+  int64_t o_stride;
+  int o_ld;
+  float* inv;         // 1 / (||U||_F + eps) per matrix
+  float decay, step;  // W <- decay W - step O
+  int vec;            // cols % 8 == 0, bstride % 8 == 0, G / M / W 16-byte aligned
+  int ovec;           // cols % 8 == 0, o_ld % 8 == 0, o_stride % 8 == 0, O 16-byte aligned
+};
+
+struct SmallLaunch {
+  int ngroups;
+  int prefix[kMaxProbs + 1];  // matrix prefix over groups
+  SmallGroup g[kMaxProbs];
+  float mu;
+  int nesterov;
+  float eps;
+  int steps;
+  float a, b, c;
+};
+
 // Launchers (defined next to their kernels).  Each returns hipGetLastError().
 hipError_t launch_momentum_norm(const MomentumLaunch& L, int grad_dtype, int nblocks, hipStream_t s);
 hipError_t launch_norm_finalize(const FinalizeLaunch& L, int nmats, hipStream_t s);
 hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks, hipStream_t s);
 hipError_t launch_ns_gemm_slices(const GemmLaunch& L, int stage, int nblocks, hipStream_t s);
 hipError_t launch_param_update(const UpdateLaunch& L, int param_dtype, int64_t nblocks, hipStream_t s);
+hipError_t launch_small_step(const SmallLaunch& L, int dtype, int nmats, hipStream_t s);
 hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int H, int d_head,
                             int causal, float* partial, int nqb, hipStream_t s);
 hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float logit_scale,

@@ -247,12 +247,8 @@ void ns_gemm_kernel(GemmLaunch L) {
     static_for<NCP>([&](auto c) { *reinterpret_cast<u32x4_t*>(bP + c * RPP * kPitch * 2) = rP[c]; });
     static_for<NCQ>([&](auto c) { *reinterpret_cast<u32x4_t*>(bQ + c * RPP * kPitch * 2) = rQ[c]; });
   };
-  // barrier without the workgroup fence of __syncthreads (that fence would
-  // drain the prefetch loads): this wave's LDS traffic done, then s_barrier
-  auto barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-  };
+  // LDS-only barrier: the prefetch loads stay in flight across it
+  auto barrier = [&]() { lds_barrier(); };
 
   f32x16_t acc[F][G];
   static_for<F * G>([&](auto ab) { acc[ab / G][ab % G] = f32x16_t{}; });
@@ -337,13 +333,11 @@ void ns_gemm_kernel(GemmLaunch L) {
   e.lj0 = wc0 + (lane & 31);
   bf16_t* C = p.C ? p.C + mat * p.sC : nullptr;
   bf16_t* Ct = (p.Ct && (!p.sym || ti != tj)) ? p.Ct + mat * p.sCt : nullptr;
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();                // every wave is done with the K slices
+  lds_barrier();                // every wave is done with the K slices
   if (p.Et) {
     // E[j][i] block (the transposed layout of this output block), coalesced into LDS
     copy_in<TN, TM, EPT, NT>(smem, p.Et + mat * p.sEt, p.lde, col0, row0, tid);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     e.Et = smem;
   }
   u32x2_t quad[F][G][4];
@@ -355,8 +349,7 @@ void ns_gemm_kernel(GemmLaunch L) {
   const int li0 = e.li0;                       // local row of quad (0, 0, 0)
   const int lj0 = e.lj0;                       // local column of block (., 0)
   if (p.Et) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();              // the staged E tile is read; reuse the buffer
+    lds_barrier();              // the staged E tile is read; reuse the buffer
   }
   if (Ct) {
     // transposed layout [j][i]: each quad is 4 consecutive i of one j
@@ -365,11 +358,9 @@ void ns_gemm_kernel(GemmLaunch L) {
       constexpr int A = X / (4 * G), B = (X / 4) % G, Qd = X % 4;
       *reinterpret_cast<u32x2_t*>(smem + (lj0 + 32 * B) * EPT + li0 + 32 * A + 8 * Qd) = quad[A][B][Qd];
     });
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     copy_out<TN, TM, EPT, NT>(smem, Ct, p.ldct, col0, row0, p.nvalid, p.mvalid, p.ct16 != 0, tid);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
   }
   if (C) {
     // row-major layout [i][j]
@@ -383,8 +374,7 @@ void ns_gemm_kernel(GemmLaunch L) {
       d[2 * EPC] = static_cast<bf16_t>(w[1] & 0xffff);
       d[3 * EPC] = static_cast<bf16_t>(w[1] >> 16);
     });
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     copy_out<TM, TN, EPC, NT>(smem, C, p.ldc, row0, col0, p.mvalid, p.nvalid, p.c16 != 0, tid);
   }
 }

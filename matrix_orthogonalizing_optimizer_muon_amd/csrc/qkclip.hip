@@ -98,10 +98,8 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
       *reinterpret_cast<u32x4_t*>(&sK[buf][(lrow + c * RPP) * PITCH + lcol]) = rk[SET][c];
     });
   };
-  auto barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS traffic done
-    __builtin_amdgcn_s_barrier();
-  };
+  // LDS-only barrier: the prefetch loads stay in flight across it
+  auto barrier = [&]() { lds_barrier(); };
 
   float m = -INFINITY;
 

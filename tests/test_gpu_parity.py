@@ -241,6 +241,42 @@ def test_muon_step_stages_ragged(mm, dev, dtype, ns_steps):
     check_step(mm, wl, host, devg, ws, hp)
 
 
+# Groups whose wide view is at most 128 x 256 run the whole step in one
+# workgroup per matrix (X and A in LDS); one row or column past either
+# bound goes to the tiled path.
+SMALL_EDGE_SHAPES = ((128, 256), (256, 128), (129, 256), (128, 257), (32, 32), (100, 250), (250, 1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ns_steps", [5, 2, 1])
+def test_muon_step_small_path_edges(mm, dev, dtype, ns_steps):
+    """Every stage of one step at the bounds of the single-workgroup path
+    (both sides of each bound, tall and wide, a single column), all in one
+    call so both paths run side by side."""
+    import torch
+    say(f"[step] single-workgroup bounds dtype={dtype} ns_steps={ns_steps}")
+    wl = gen.small_workload(SMALL_EDGE_SHAPES, batch=2, dtype=dtype)
+    host, devg = make_groups(wl, 17 + ns_steps, dev)
+    hp = mm.HParams(ns_steps=ns_steps)
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    check_step(mm, wl, host, devg, ws, hp)
+
+
+def test_muon_step_small_path_many_matrices(mm, dev):
+    """300 small matrices in one group (one workgroup each, more blocks than
+    compute units) next to a second small group: sampled matrices, every
+    stage, against the oracle."""
+    import torch
+    say("[step] 300 x 64x200 and 5 x 200x64")
+    wl = gen.Workload("many_small", [gen.Group("g0", 300, 64, 200), gen.Group("g1", 5, 200, 64)], "bf16")
+    host, devg = make_groups(wl, 23, dev)
+    hp = mm.HParams()
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    check_step(mm, wl, host, devg, ws, hp, sample={0: [0, 137, 299], 1: [0, 4]})
+
+
 def test_muon_step_sixteen_groups(mm, dev):
     """The largest call the boundary accepts: MUON_MAX_GROUPS groups of
     assorted ragged shapes (tall, wide, square, a single row or column, both
