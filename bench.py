@@ -204,6 +204,13 @@ def main():
             t = prof[k][0] / prof[k][1] * 1e-3
             hbm[k] = {"GBs": round(by / t / 1e9, 1), "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
                       "bytes": by, "traffic": round(traffic[k]) if k in traffic else None}
+    if prof["qk_rescale"][1]:
+        # the clipped heads' rows of W_q and W_k, each read and written once
+        # (bf16); 59 MB per step here, so the pass is launch-bound
+        by = int((clipped == 1).sum()) * D * dm * 2 * 2 * 2
+        t = prof["qk_rescale"][0] / prof["qk_rescale"][1] * 1e-3
+        hbm["qk_rescale"] = {"GBs": round(by / t / 1e9, 1), "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+                             "bytes": by, "traffic": round(traffic["qk_rescale"]) if "qk_rescale" in traffic else None}
     if prof["qk_rowmax"][1]:
         qk_flop = 2 * D * B * H * T * (T + 1) / 2
         t = prof["qk_rowmax"][0] / prof["qk_rowmax"][1] * 1e-3

@@ -21,7 +21,8 @@ Sources (web pages, cited by title and section):
         "The exploding-logit problem", "MuonClip: QK-clip, per head, adapted
         to MLA".
   [MS]  "About Muon: Muon At Scale" (kiungsong.github.io), sections
-        "Why Not Bernstein's Multiplier?", "When Softmax Collapses".
+        "Why Not Bernstein's Multiplier?", "When Softmax Collapses",
+        "What Breaks at Scale" (subsection "The Matrix Does Not Fit": Dion).
 
 Readings taken where the pages are silent:
   * Nesterov lookahead: U = G + mu * M_new (sum-form momentum, [MC] 02 says a
@@ -37,6 +38,10 @@ Readings taken where the pages are silent:
     causal pairs j <= i (diagonal included), per head.
   * Clip tie/non-finite: a head is clipped iff S_max > tau; a NaN/Inf S_max
     leaves the weights untouched and is flagged -1.
+  * Dion: "orthogonalize P" is the Q factor of the thin QR with a positive
+    diagonal; ColNorm leaves a zero column zero; the update X - lr P Q'^T has
+    no scale factor or weight decay (the pages write none); Q is state the
+    caller keeps between steps (the warm start).
 
 Pins: every function here is checked in tests/test_oracle_*.py against
 closed forms, printed worked examples, textbook special cases and brute force
@@ -342,3 +347,50 @@ def adamw_step(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, *,
     vhat = v / (1.0 - beta2 ** step)
     p = p * (1.0 - lr * weight_decay) - lr * mhat / (np.sqrt(vhat) + eps)
     return p, m, v
+
+
+# ---------------------------------------------------------------------------
+# Dion: the rank-r orthonormalised update ([MS] "What Breaks at Scale",
+# subsection "The Matrix Does Not Fit").
+# ---------------------------------------------------------------------------
+
+
+def orthonormal_basis(P0: np.ndarray) -> np.ndarray:
+    """The Q factor of the thin QR of P0 with a non-negative diagonal of R:
+    the Gram-Schmidt basis of P0's columns in order.  [MS] says "orthogonalize
+    P" without naming the method; this is the plainest reading and the basis
+    every QR or Cholesky-QR variant converges to.  Library QR as the step."""
+    Qf, Rf = np.linalg.qr(np.asarray(P0, dtype=np.float64), mode="reduced")
+    sgn = np.sign(np.diag(Rf))
+    sgn[sgn == 0] = 1.0
+    return Qf * sgn[None, :]
+
+
+def column_normalize(R: np.ndarray) -> np.ndarray:
+    """ColNorm: every column divided by its l2 norm; a zero column stays zero
+    (the pages give no epsilon)."""
+    R = np.asarray(R, dtype=np.float64)
+    nrm = np.linalg.norm(R, axis=0)
+    safe = np.where(nrm > 0.0, nrm, 1.0)
+    return np.where(nrm[None, :] > 0.0, R / safe[None, :], 0.0)
+
+
+def dion_step(X: np.ndarray, G: np.ndarray, M: np.ndarray, Q: np.ndarray, *,
+              mu: float, lr: float):
+    """One Dion step on an m x n matrix with rank-r state Q (n x r), float64:
+        B = M + G
+        P = orth(B Q)                 (one warm-started power step ...
+        R = B^T P                      ... PowerIter_1(B; Q))
+        M' = B - (1 - mu) P R^T       (error feedback: the rank-r piece leaves M)
+        Q' = ColNorm(R)
+        X' = X - lr P Q'^T
+    in the pages' order and notation.  No scale factor or weight decay: the
+    pages' update has neither.  Returns (X', M', Q', P, R)."""
+    X = np.asarray(X, dtype=np.float64)
+    B = np.asarray(M, dtype=np.float64) + np.asarray(G, dtype=np.float64)
+    P = orthonormal_basis(B @ np.asarray(Q, dtype=np.float64))
+    R = B.T @ P
+    M_new = B - (1.0 - mu) * (P @ R.T)
+    Q_new = column_normalize(R)
+    X_new = X - lr * (P @ Q_new.T)
+    return X_new, M_new, Q_new, P, R
