@@ -31,6 +31,7 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16
 # 2.07-2.10 GHz under that load
 MFMA_BF16_MEASURED_TFLOPS = 2120.0
 HBM_PEAK_GBS = 8000.0
+MFMA_FP32_PEAK_TFLOPS = 157.3    # dense fp32 MFMA, the spec figure
 
 
 def parse():
@@ -253,6 +254,7 @@ def main():
         k = max(2, min(3, args.steps))
         out["other_configs"] = {"dense_decoder_24_layers": config_reading(mm, torch, dev, seed, 3, k, 1),
                                 "moe_64_experts": config_reading(mm, torch, dev, seed, 4, k, 1)}
+        out["dion_rank128"] = dion_reading(mm, torch, dev, seed)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
     print(json.dumps(out), flush=True)
@@ -333,6 +335,66 @@ def small_matrix_reading(mm, torch, dev, seed, steps=200, warmup=20):
             "graph_us_per_step": round(1e6 * el_graph / steps, 2),
             "kernels_us_per_step": {k: round(1e3 * v[0] / steps, 2) for k, v in prof.items() if v[1]},
             "launches_per_step": sum(v[1] for v in prof.values()) / steps}
+
+
+def dion_reading(mm, torch, dev, seed, batch=48, size=4096, rank=128, steps=3):
+    """Dion's rank-r step next to the Muon step on the same group: 48 bf16
+    4096 x 4096 matrices (the square class of the 24-layer decoder; 4096^2 is
+    the pages' own example size for Dion's traffic), rank 128, fp32 momentum,
+    N(0,1) gradients, Q column-normalised Gaussian.  Flops per matrix: the
+    products B Q and B^T P (2 m n r each), P L^-T twice (2 m r^2 each) and the
+    update's two rank-r products (4 m n r): 8 m n r + 4 m r^2."""
+    from synthetic import generators as gen
+    shape = (batch, size, size)
+    W = gen.bulk_normal_torch(shape, 0.02, seed + 600, dev, torch.bfloat16)
+    G = gen.bulk_normal_torch(shape, 1.0, seed + 601, dev, torch.bfloat16)
+    M = gen.bulk_normal_torch(shape, 0.5, seed + 602, dev, torch.float32)
+    Q = gen.bulk_normal_torch((batch, size, rank), 1.0, seed + 603, dev, torch.float32)
+    Q /= Q.norm(dim=1, keepdim=True)
+    ws = torch.empty(max(mm.load_library().dion_workspace_size(batch, size, size, rank), 256),
+                     dtype=torch.uint8, device=dev)
+    mm.dion_step(W, G, M, Q, lr=0.02, mu=0.95, workspace=ws)
+    torch.cuda.synchronize()
+    mm.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mm.dion_step(W, G, M, Q, lr=0.02, mu=0.95, workspace=ws)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    prof = mm.profile_collect()
+    mm.profile_enable(False)
+    del ws
+    torch.cuda.empty_cache()
+    m = n = size
+    flop = batch * (8.0 * m * n * rank + 4.0 * m * rank * rank)
+    kflop = {"dion_bq": 2.0 * m * n * rank, "dion_btp": 2.0 * m * n * rank, "dion_update": 4.0 * m * n * rank,
+             "dion_pl": 2.0 * m * rank * rank}
+    kern = {}
+    for k, v in prof.items():
+        if not v[1]:
+            continue
+        kern[k] = {"ms_per_step": round(v[0] / steps, 4), "launches_per_step": v[1] / steps}
+        if k in kflop:
+            tf = batch * kflop[k] * (v[1] / steps) / (v[0] / steps * 1e-3) / 1e12
+            kern[k]["tflops_fp32"] = round(tf, 1)
+            kern[k]["frac_fp32_mfma_peak"] = round(tf / MFMA_FP32_PEAK_TFLOPS, 4)
+    # the Muon step on the same group, for the comparison the pages make
+    hp = mm.HParams(lr=0.02, momentum=0.95, weight_decay=0.0)
+    mws = torch.empty(mm.workspace_size([(W, G, M)]), dtype=torch.uint8, device=dev)
+    mm.muon_step([(W, G, M)], hp, workspace=mws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mm.muon_step([(W, G, M)], hp, workspace=mws)
+    torch.cuda.synchronize()
+    el_muon = time.perf_counter() - t0
+    del W, G, M, Q, mws
+    torch.cuda.empty_cache()
+    return {"workload": f"{batch} x {size}x{size} bf16, rank {rank}", "steps": steps,
+            "dion_ms_per_step": round(1e3 * el / steps, 3), "dion_steps_per_s": round(steps / el, 3),
+            "dion_tflops_fp32": round(flop / (el / steps) / 1e12, 1),
+            "muon_ms_per_step_same_group": round(1e3 * el_muon / steps, 3),
+            "kernels": kern}
 
 
 def config_reading(mm, torch, dev, seed, idx, steps, warmup):

@@ -11,7 +11,8 @@
  *        "The Muon optimizer", "The exploding-logit problem",
  *        "MuonClip: QK-clip, per head, adapted to MLA".
  *   [MS] "About Muon: Muon At Scale" — "Why Not Bernstein's Multiplier?",
- *        "When Softmax Collapses".
+ *        "When Softmax Collapses", "What Breaks at Scale" ("The Matrix Does
+ *        Not Fit": Dion).
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers unless stated otherwise; the structs
@@ -267,6 +268,33 @@ typedef struct {
 } adamw_tensor_t;
 int adamw_step(const adamw_tensor_t* tensors, int n_tensors, int dtype,
                const adamw_hparams_t* hp, hipStream_t stream);
+
+/* ----------------------------------------------------------------- dion_step
+ * One rank-r Dion step ([MS] "What Breaks at Scale", "The Matrix Does Not
+ * Fit") on each of `batch` matrices (param and grad of `dtype`, [rows][cols],
+ * batch_stride elements apart; momentum fp32 with the same layout):
+ *   B = M + G;  P = orth(B Q);  R = B^T P;
+ *   M <- B - (1 - mu) P R^T;  Q <- ColNorm(R);  W <- W - lr P Q^T
+ *   q:      fp32 [batch][cols][rank], dense, the caller's state between steps
+ *           (the power step's warm start): read, then replaced by ColNorm(R).
+ *   orth:   the basis of the thin QR of B Q with a positive diagonal,
+ *           computed by Cholesky-QR applied twice (Gram matrices and their
+ *           Cholesky factors in fp64, products in fp32).  A direction the
+ *           columns of B Q do not add (pivot <= 1e-10 x the largest diagonal
+ *           entry of the Gram matrix) gets a zero column of P, so it takes no
+ *           update and its column of Q becomes zero.
+ *   ColNorm: each column of R over its l2 norm; a zero column stays zero.
+ *   No scale factor or weight decay (the pages' update has neither).
+ *   Arithmetic fp32 (momentum, products, update), param rounded once (RNE).
+ * Requirements (else MUON_ERR_UNSUPPORTED): rank a multiple of 8 in 8..128,
+ * rank <= min(rows, cols); rows and cols multiples of 8; batch_stride a
+ * multiple of 8; every pointer 16-byte aligned.  Other argument errors:
+ * MUON_ERR_INVALID_ARG; a missing or short workspace: MUON_ERR_WORKSPACE.   */
+size_t dion_workspace_size(int batch, int rows, int cols, int rank);
+int dion_step(void* param, int dtype, const void* grad, float* momentum, float* q,
+              int batch, int rows, int cols, int rank, int64_t batch_stride,
+              float lr, float mu, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
 
 /* -------------------------------------------------------------- diagnostics */
 const char* muon_status_string(int status);

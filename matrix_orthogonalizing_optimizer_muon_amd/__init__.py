@@ -110,6 +110,10 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
     lib.attn_fwd.restype = i32
     lib.adamw_step.argtypes = [ctypes.POINTER(_AdamWTensor), i32, i32, ctypes.POINTER(_AdamWHParams), vp]
+    lib.dion_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.dion_workspace_size.restype = sz
+    lib.dion_step.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i64, f32, f32, vp, sz, vp]
+    lib.dion_step.restype = i32
     lib.adamw_step.restype = i32
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
@@ -472,6 +476,31 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, beta1: float 
     hp = _AdamWHParams(lr, beta1, beta2, eps, weight_decay, step)
     _check(lib.adamw_step(arr, n, dtype if dtype is not None else DTYPE_F32, ctypes.byref(hp), _stream()),
            "adamw_step")
+
+
+def dion_step(param, grad, momentum, q, *, lr: float, mu: float = 0.95, workspace=None):
+    """One rank-r Dion step in place: param and grad ([rows, cols] or
+    [batch, rows, cols], fp32 or bf16, same dtype), momentum fp32 of the same
+    shape, q fp32 [cols, rank] or [batch, cols, rank] (the warm-start state,
+    replaced by ColNorm(R)).  rank = q.shape[-1]."""
+    torch = _torch()
+    lib = load_library()
+    _need_cuda(param, grad, momentum, q)
+    b, r, c, st = _as3d(param)
+    if grad.dtype != param.dtype or momentum.dtype != torch.float32 or q.dtype != torch.float32:
+        raise TypeError("grad must match the param dtype; momentum and q must be float32")
+    if _as3d(grad) != (b, r, c, st) or _as3d(momentum) != (b, r, c, st):
+        raise ValueError("param, grad and momentum must share shape and strides")
+    rank = q.shape[-1]
+    if not q.is_contiguous() or q.numel() != b * c * rank or q.shape[-2] != c:
+        raise ValueError("q must be a contiguous [batch, cols, rank] float32 tensor")
+    need = int(lib.dion_workspace_size(b, r, c, rank))
+    if workspace is None:
+        workspace = _workspace(need, param.device)
+    _check(lib.dion_step(param.data_ptr(), _dtype_code(param), grad.data_ptr(), momentum.data_ptr(),
+                         q.data_ptr(), b, r, c, rank, st, lr, mu, workspace.data_ptr(), workspace.numel(),
+                         _stream()), "dion_step")
+    return workspace
 
 
 def profile_enable(on: bool = True):

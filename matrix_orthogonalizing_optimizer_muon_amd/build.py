@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuon.so")
-SOURCES = ["api.hip", "elementwise.hip", "ns_gemm.hip", "small.hip", "qkclip.hip", "adamw.hip", "attention.hip"]
+SOURCES = ["api.hip", "elementwise.hip", "ns_gemm.hip", "small.hip", "dion.hip", "qkclip.hip", "adamw.hip", "attention.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.

@@ -711,6 +711,131 @@ int attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int
   return MUON_OK;
 }
 
+// ----------------------------------------------------------------------------
+// Dion
+// ----------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+struct DionPlan {
+  int rp, nsplit;
+  size_t gram_per;  // doubles per matrix in the Gram region
+  size_t off_pa, off_pb, off_r, off_lt, off_inv, off_gram, total;
+};
+
+bool dion_dims_ok(int batch, int rows, int cols, int rank) {
+  if (batch < 1 || rows < 1 || cols < 1 || rank < 1) return false;
+  if (rows > (1 << 20) || cols > (1 << 20)) return false;
+  return static_cast<int64_t>(rows) * cols < (int64_t(1) << 31);
+}
+
+DionPlan dion_plan(int batch, int rows, int cols, int rank) {
+  DionPlan d{};
+  d.rp = round_up(rank, 32);
+  d.nsplit = (rows + 127) / 128;
+  size_t c = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = c;
+    c = align_up(c + bytes);
+    return o;
+  };
+  const size_t b = static_cast<size_t>(batch), rp = static_cast<size_t>(d.rp);
+  d.off_pa = take(b * rows * rp * sizeof(float));
+  d.off_pb = take(b * rows * rp * sizeof(float));
+  d.off_r = take(b * cols * rp * sizeof(float));
+  d.off_lt = take(b * rp * rp * sizeof(float));
+  d.off_inv = take(b * rp * sizeof(float));
+  // Gram partials, later the column sums of squares of R per 64 rows
+  d.gram_per = std::max(static_cast<size_t>(d.nsplit) * rp * rp, static_cast<size_t>((cols + 63) / 64) * rp);
+  d.off_gram = take(b * d.gram_per * sizeof(double));
+  d.total = c;
+  return d;
+}
+}  // namespace
+
+extern "C" {
+
+size_t dion_workspace_size(int batch, int rows, int cols, int rank) {
+  if (!dion_dims_ok(batch, rows, cols, rank)) return 0;
+  return dion_plan(batch, rows, cols, rank).total;
+}
+
+int dion_step(void* param, int dtype, const void* grad, float* momentum, float* q, int batch, int rows, int cols,
+              int rank, int64_t batch_stride, float lr, float mu, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  if (!param || !grad || !momentum || !q) return MUON_ERR_INVALID_ARG;
+  if (dtype != MUON_DTYPE_F32 && dtype != MUON_DTYPE_BF16) return MUON_ERR_INVALID_ARG;
+  if (!dion_dims_ok(batch, rows, cols, rank)) return MUON_ERR_INVALID_ARG;
+  if (batch_stride < static_cast<int64_t>(rows) * cols) return MUON_ERR_INVALID_ARG;
+  if (!isfinite(lr) || !isfinite(mu)) return MUON_ERR_INVALID_ARG;
+  if (rank % 8 != 0 || rank > 128 || rank > std::min(rows, cols) || rows % 8 != 0 || cols % 8 != 0 ||
+      batch_stride % 8 != 0 || batch > 65535 || !aligned(param, 16) || !aligned(grad, 16) ||
+      !aligned(momentum, 16) || !aligned(q, 16))
+    return MUON_ERR_UNSUPPORTED;
+  const DionPlan d = dion_plan(batch, rows, cols, rank);
+  if (!workspace || workspace_bytes < d.total || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
+
+  DionArgs A{};
+  A.G = grad;
+  A.M = momentum;
+  A.W = param;
+  A.Q = q;
+  A.bstride = batch_stride;
+  A.q_stride = static_cast<int64_t>(cols) * rank;
+  A.m = rows;
+  A.n = cols;
+  A.r = rank;
+  A.rp = d.rp;
+  A.nsplit = d.nsplit;
+  A.mu = mu;
+  A.lr = lr;
+  float* Pa = at<float>(workspace, d.off_pa);
+  float* Pb = at<float>(workspace, d.off_pb);
+  const int64_t ps = static_cast<int64_t>(rows) * d.rp;
+  A.R = at<float>(workspace, d.off_r);
+  A.r_stride = static_cast<int64_t>(cols) * d.rp;
+  A.Lt = at<float>(workspace, d.off_lt);
+  A.lt_stride = static_cast<int64_t>(d.rp) * d.rp;
+  A.inv = at<float>(workspace, d.off_inv);
+  A.gram = at<double>(workspace, d.off_gram);
+  A.gram_stride = static_cast<int64_t>(d.gram_per);
+
+  // P0 = B Q
+  A.dst = Pa;
+  A.dst_stride = ps;
+  MUON_LAUNCH(KIND_DION_BQ, stream, launch_dion_gemm(A, DION_BQ, dtype, batch, stream));
+  // Cholesky-QR, twice: Pa -> Pb -> Pa
+  for (int pass = 0; pass < 2; ++pass) {
+    float* from = pass == 0 ? Pa : Pb;
+    float* to = pass == 0 ? Pb : Pa;
+    A.src = from;
+    A.src_stride = ps;
+    MUON_LAUNCH(KIND_DION_GRAM, stream, launch_dion_gram(A, batch, stream));
+    MUON_LAUNCH(KIND_DION_GRAM, stream, launch_dion_gram_reduce(A, batch, stream));
+    MUON_LAUNCH(KIND_DION_CHOL, stream, launch_dion_chol(A, batch, stream));
+    A.bsrc = A.Lt;
+    A.bsrc_stride = A.lt_stride;
+    A.dst = to;
+    A.dst_stride = ps;
+    MUON_LAUNCH(KIND_DION_PL, stream, launch_dion_gemm(A, DION_PL, dtype, batch, stream));
+  }
+  // R = B^T P
+  A.bsrc = Pa;
+  A.bsrc_stride = ps;
+  A.dst = A.R;
+  A.dst_stride = A.r_stride;
+  MUON_LAUNCH(KIND_DION_BTP, stream, launch_dion_gemm(A, DION_BTP, dtype, batch, stream));
+  // column norms, Q = ColNorm(R)
+  MUON_LAUNCH(KIND_DION_COLNORM, stream, launch_dion_colnorm(A, batch, stream));
+  // M <- B - (1 - mu) P R^T, W <- W - lr P Q^T
+  A.src = Pa;
+  A.src_stride = ps;
+  A.bsrc = A.R;
+  A.bsrc_stride = A.r_stride;
+  MUON_LAUNCH(KIND_DION_UPDATE, stream, launch_dion_gemm(A, DION_UPD, dtype, batch, stream));
+  return MUON_OK;
+}
+
 int muon_profile_enable(int on) {
   for (auto& r : g_prof) {
     g_event_pool.push_back(r.a);
@@ -742,7 +867,9 @@ const char* muon_kernel_kind_name(int kind) {
   static const char* names[KIND_COUNT] = {"momentum_norm", "norm_finalize", "ns_syrk_xxt", "ns_syrk_poly",
                                           "ns_gemm_bx",    "param_update",  "qk_rowmax",   "qk_reduce",
                                           "qk_rescale",    "adamw",         "attn_fwd",
-                                          "ns_syrk_xxt_slices", "ns_syrk_poly_slices", "small_step"};
+                                          "ns_syrk_xxt_slices", "ns_syrk_poly_slices", "small_step",
+                                          "dion_bq",       "dion_gram",     "dion_chol",   "dion_pl",
+                                          "dion_btp",      "dion_colnorm",  "dion_update"};
   if (kind < 0 || kind >= KIND_COUNT) return "unknown";
   return names[kind];
 }

@@ -81,7 +81,14 @@ enum KernelKind {
   KIND_NS_SYRK_SLICES = 11,
   KIND_NS_POLY_SLICES = 12,
   KIND_SMALL_STEP = 13,
-  KIND_COUNT = 14
+  KIND_DION_BQ = 14,
+  KIND_DION_GRAM = 15,
+  KIND_DION_CHOL = 16,
+  KIND_DION_PL = 17,
+  KIND_DION_BTP = 18,
+  KIND_DION_COLNORM = 19,
+  KIND_DION_UPDATE = 20,
+  KIND_COUNT = 21
 };
 
 // ---------------------------------------------------------------------------
@@ -211,6 +218,35 @@ struct SmallLaunch {
   float a, b, c;
 };
 
+// Dion's rank-r step: one argument block for every launch of a step; the
+// GEMM launches set src / bsrc / dst to their operands.
+enum DionMode { DION_BQ = 0, DION_PL = 1, DION_BTP = 2, DION_UPD = 3 };
+
+struct DionArgs {
+  const void* G;       // grad (param dtype), [m][n] per matrix
+  float* M;            // momentum fp32
+  void* W;             // param
+  float* Q;            // rank state fp32 [n][r] per matrix, dense
+  int64_t bstride;     // elements between matrices of G / M / W
+  int64_t q_stride;    // n * r
+  int m, n, r, rp;     // rp = r rounded up to 32
+  int nsplit;          // Gram partials per matrix (row chunks of 128)
+  float mu, lr;
+  const float* src;    // GEMM A operand (P0 / P), [m][rp]
+  int64_t src_stride;
+  const float* bsrc;   // GEMM B operand (L^-T [rp][rp], P [m][rp] or R [n][rp])
+  int64_t bsrc_stride;
+  float* dst;          // GEMM output [rows][rp]
+  int64_t dst_stride;
+  float* R;            // [n][rp]
+  int64_t r_stride;
+  float* Lt;           // [rp][rp]
+  int64_t lt_stride;
+  float* inv;          // [rp] per matrix: 1 / column norm of R
+  double* gram;        // [nsplit][rp][rp] per matrix
+  int64_t gram_stride;
+};
+
 // Launchers (defined next to their kernels).  Each returns hipGetLastError().
 hipError_t launch_momentum_norm(const MomentumLaunch& L, int grad_dtype, int nblocks, hipStream_t s);
 hipError_t launch_norm_finalize(const FinalizeLaunch& L, int nmats, hipStream_t s);
@@ -218,6 +254,11 @@ hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks,
 hipError_t launch_ns_gemm_slices(const GemmLaunch& L, int stage, int nblocks, hipStream_t s);
 hipError_t launch_param_update(const UpdateLaunch& L, int param_dtype, int64_t nblocks, hipStream_t s);
 hipError_t launch_small_step(const SmallLaunch& L, int dtype, int nmats, hipStream_t s);
+hipError_t launch_dion_gemm(const DionArgs& A, int mode, int dtype, int batch, hipStream_t s);
+hipError_t launch_dion_gram(const DionArgs& A, int batch, hipStream_t s);
+hipError_t launch_dion_gram_reduce(const DionArgs& A, int batch, hipStream_t s);
+hipError_t launch_dion_chol(const DionArgs& A, int batch, hipStream_t s);
+hipError_t launch_dion_colnorm(const DionArgs& A, int batch, hipStream_t s);
 hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int H, int d_head,
                             int causal, float* partial, int nqb, hipStream_t s);
 hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float logit_scale,

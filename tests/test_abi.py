@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["muon_step", "ns_orthogonalize", "qkclip_rowmax", "qkclip_rescale",
-              "qkclip_rescale_slices", "qkclip_rescale_mla", "adamw_step", "attn_fwd"]:
+              "qkclip_rescale_slices", "qkclip_rescale_mla", "adamw_step", "attn_fwd", "dion_step"]:
         assert n in names
 
 
@@ -121,3 +121,31 @@ def test_workspace_layout_query(lib):
     assert lib.muon_step_workspace_layout(g, 2, 2, 5, ctypes.byref(lay)) == mm.MUON_ERR_INVALID_ARG
     total = lib.muon_step_workspace_size(g, 2)
     assert lay.o_offset < total
+
+
+def test_dion_host_validation_without_gpu(lib):
+    """dion_step's argument checks run on the host: invalid arguments,
+    unsupported shapes and a missing workspace are reported before any launch
+    (the fake device pointers are never dereferenced)."""
+    import matrix_orthogonalizing_optimizer_muon_amd as mm
+    P = 1 << 12           # 16-byte aligned fake pointer, never touched
+    ok = dict(dtype=mm.DTYPE_BF16, batch=2, rows=64, cols=96, rank=16, stride=64 * 96, lr=0.01, mu=0.95)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.dion_step(a.get("p", P), a["dtype"], a.get("g", P), a.get("m", P), a.get("q", P), a["batch"],
+                             a["rows"], a["cols"], a["rank"], a["stride"], a["lr"], a["mu"], a.get("ws", None),
+                             a.get("wsz", 0), None)
+    assert lib.dion_workspace_size(2, 64, 96, 16) > 0
+    assert lib.dion_workspace_size(0, 64, 96, 16) == 0
+    assert call(p=None) == mm.MUON_ERR_INVALID_ARG
+    assert call(dtype=7) == mm.MUON_ERR_INVALID_ARG
+    assert call(stride=64 * 96 - 8) == mm.MUON_ERR_INVALID_ARG
+    assert call(lr=float("nan")) == mm.MUON_ERR_INVALID_ARG
+    assert call(rank=12) == mm.MUON_ERR_UNSUPPORTED          # not a multiple of 8
+    assert call(rank=136, rows=256, cols=256, stride=65536) == mm.MUON_ERR_UNSUPPORTED   # above 128
+    assert call(rank=72) == mm.MUON_ERR_UNSUPPORTED          # above min(rows, cols)
+    assert call(cols=100, stride=6400) == mm.MUON_ERR_UNSUPPORTED
+    assert call(q=P + 4) == mm.MUON_ERR_UNSUPPORTED          # misaligned
+    assert call() == mm.MUON_ERR_WORKSPACE
+    assert call(ws=P, wsz=lib.dion_workspace_size(2, 64, 96, 16) - 1) == mm.MUON_ERR_WORKSPACE
