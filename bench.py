@@ -82,6 +82,11 @@ def ns_flops(m, n):
     return {"ns_syrk_xxt": m * (m + 1) * n, "ns_syrk_poly": m * m * (m + 1), "ns_gemm_bx": 2 * m * m * n}
 
 
+def note(msg):
+    """A progress line on stderr (the JSON result alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -244,17 +249,24 @@ def main():
         "heads_clipped_per_step": n_clipped,
     }
 
+    note("MuonClip layer step timed")
     out["companion"] = companion(mm, torch, dev, seed, n_mats * m * n)
     out["companion"]["attn_fwd"] = attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, prof["qk_rowmax"])
     del Q, K, Wqkv, Wo, Gqkv, Go, Mqkv, Mo, ws, groups
     torch.cuda.empty_cache()
+    note("companion passes timed")
     out["layer_hidden2048"] = config_reading(mm, torch, dev, seed, 2, args.steps, args.warmup)
+    note("hidden-2048 layer timed")
     out["single_matrix_256x128"] = small_matrix_reading(mm, torch, dev, seed)
+    note("single 256x128 matrix timed")
     if not args.no_other_configs:
         k = max(2, min(3, args.steps))
-        out["other_configs"] = {"dense_decoder_24_layers": config_reading(mm, torch, dev, seed, 3, k, 1),
-                                "moe_64_experts": config_reading(mm, torch, dev, seed, 4, k, 1)}
+        out["other_configs"] = {"dense_decoder_24_layers": config_reading(mm, torch, dev, seed, 3, k, 1)}
+        note("24-layer decoder timed")
+        out["other_configs"]["moe_64_experts"] = config_reading(mm, torch, dev, seed, 4, k, 1)
+        note("64-expert MoE stack timed")
         out["dion_rank128"] = dion_reading(mm, torch, dev, seed)
+        note("Dion step timed")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
     print(json.dumps(out), flush=True)

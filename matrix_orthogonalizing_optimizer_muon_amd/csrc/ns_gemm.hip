@@ -6,11 +6,11 @@
 // Every product of the iteration is an "NT" contraction whose two operands
 // are row-major with the contraction index contiguous:
 //   A = X X^T                P = Q = X  (m x n),  K = n, symmetric output
-//   B = a I + b A + c A A^T  P = Q = A  (m x m),  K = m, symmetric output (A = A^T)
-//   X' = B X                 P = B,  Q = X^T (n x m), K = m
-// (a X + (b A + c A A) X is computed as (a I + b A + c A A) X: one rounding of
-// the polynomial matrix, no a X term in the last product.)
+//   B = b A + c A A^T        P = Q = A  (m x m),  K = m, symmetric output (A = A^T)
+//   X' = a X + B X           P = B,  Q = X^T (n x m), K = m
 // so both MFMA operands are 16-byte row segments, staged through LDS.  The
+// b A and a X terms are added in fp32 in the epilogue, from the stored bf16
+// A and X (folding a I into B would round a + B_ii to bf16).  The
 // symmetric products compute only tiles ti <= tj and write each off-diagonal
 // tile twice (in place and mirrored).  X is kept in both layouts (X and X^T):
 // the epilogue of X' writes both, so no transpose pass is ever needed.
