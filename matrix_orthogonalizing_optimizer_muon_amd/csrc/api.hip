@@ -314,12 +314,19 @@ int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c,
       for (int tile : {256, 128}) {
         GemmLaunch L{};
         int tiles = 0;
-        for (size_t g = 0; g < plans.size(); ++g) {
-          if (plans[g].tile != tile) continue;
+        // problems by decreasing contraction length, so that the blocks
+        // dispatched last, which set the launch's tail, are the shortest
+        std::vector<int> order;
+        for (size_t g = 0; g < plans.size(); ++g)
+          if (plans[g].tile == tile) order.push_back(static_cast<int>(g));
+        auto klen = [&](int g) { return stage == STAGE_SYRK ? plans[g].np : plans[g].mp; };
+        std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return klen(x) > klen(y); });
+        for (int g : order) {
           GemmProb q = make_prob(plans[g], stage, t, steps, a, b, c, ws, fins ? &(*fins)[g] : nullptr);
+          q.ntiles = plans[g].batch * q.tiles_per_mat;
           L.prefix[L.nprob] = tiles;
           L.p[L.nprob] = q;
-          tiles += plans[g].batch * q.tiles_per_mat;
+          tiles += (q.ntiles + 7) / 8 * 8;
           ++L.nprob;
         }
         if (L.nprob == 0) continue;

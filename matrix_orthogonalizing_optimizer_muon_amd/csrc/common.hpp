@@ -112,6 +112,7 @@ struct GemmProb {
   int K;                         // contraction length, multiple of 32
   int tm, tn;                    // tiles along i and j
   int tiles_per_mat;
+  int ntiles;       // batch * tiles_per_mat
   int sym;          // 1: only tiles ti <= tj, written at (ti,tj) and mirrored
   int alpha_pow;    // 0: s = 1, 1: s = alpha, 2: s = alpha^2
   int mvalid, nvalid;  // outputs are written only for i < mvalid, j < nvalid
@@ -124,7 +125,8 @@ struct GemmLaunch {
   int nprob;
   int band;         // non-symmetric products with tn % 8 == 0: column bands per XCD
   int lin0;         // column-slice launches: first tile (in the launch's tile order) covered
-  int prefix[kMaxProbs + 1];
+  int prefix[kMaxProbs + 1];  // launch-index range of each problem: ntiles rounded up to a
+                               // multiple of 8 (the padding blocks exit at once)
   GemmProb p[kMaxProbs];
 };
 

@@ -137,20 +137,27 @@ void ns_gemm_kernel(GemmLaunch L) {
   auto sQ = [&](int buf) { return smem + 2 * TM * kPitch + buf * TN * kPitch; };
 
   // ---- block -> (problem, matrix, tile, column slice)
-  int lin, slice = 0;
+  int vb, slice = 0;
   if (NSLICE == 1) {
-    lin = L.band ? static_cast<int>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    vb = blockIdx.x;
   } else {
     // the slices of one tile are adjacent in each XCD's contiguous range, so
     // they mostly share that XCD's cache for the common P panel
     const int r = xcd_remap(blockIdx.x, gridDim.x);
-    lin = L.lin0 + r / NSLICE;
+    vb = L.lin0 + r / NSLICE;
     slice = r % NSLICE;
   }
   int gi = 0;
-  while (gi + 1 < L.nprob && lin >= L.prefix[gi + 1]) ++gi;
+  while (gi + 1 < L.nprob && vb >= L.prefix[gi + 1]) ++gi;
   const GemmProb& p = L.p[gi];
-  const int local = lin - L.prefix[gi];
+  // Each problem's index range is a multiple of 8 long, so index b runs on
+  // XCD b % 8 whatever problem it falls in; inside a problem each XCD takes
+  // one contiguous eighth of its tiles (column bands: see below).  Every XCD
+  // thus gets the same share of each problem, whatever their contraction
+  // lengths.
+  const int lb = vb - L.prefix[gi];
+  const int local = L.band ? lb : xcd_remap(lb, L.prefix[gi + 1] - L.prefix[gi]);
+  if (local >= p.ntiles) return;   // padding of the problem's range
   int mat = local / p.tiles_per_mat;
   int t = local - mat * p.tiles_per_mat;
   int ti, tj;
