@@ -263,6 +263,21 @@ def test_muon_step_small_path_edges(mm, dev, dtype, ns_steps):
     check_step(mm, wl, host, devg, ws, hp)
 
 
+def test_muon_step_mixed_contraction_lengths(mm, dev):
+    """256-tile groups whose X X^T products differ 4x in contraction length,
+    in one launch per stage: problems ordered by contraction length, each
+    problem's block range padded to a multiple of 8 (the padding blocks exit
+    at once).  Every stage of every matrix against the oracle."""
+    import torch
+    say("[step] 2 x 512x512 with 512x2048 and 2048x512 (X X^T over K = 512 and 2048)")
+    wl = gen.small_workload(((512, 512), (512, 2048), (2048, 512)), batch=2, dtype="bf16")
+    host, devg = make_groups(wl, 29, dev)
+    hp = mm.HParams()
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    check_step(mm, wl, host, devg, ws, hp)
+
+
 def test_muon_step_small_path_many_matrices(mm, dev):
     """300 small matrices in one group (one workgroup each, more blocks than
     compute units) next to a second small group: sampled matrices, every
