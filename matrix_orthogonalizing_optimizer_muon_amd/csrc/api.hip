@@ -189,11 +189,12 @@ int launch_prep(const std::vector<Plan>& plans, const std::vector<PrepIn>& ins, 
     q.tiles_r = p.tiles_r;
     q.tiles_c = p.tiles_c;
     q.tiles_per_mat = p.mom_tiles;
+    q.pairs_c = (p.tiles_c + 1) / 2;
     q.batch = p.batch;
     q.vec = (p.cols % 4 == 0) && (p.bstride % 4 == 0) && aligned(q.G, 4 * esz) &&
             (q.M == nullptr || aligned(q.M, 16));
     L.prefix[g] = blocks;
-    blocks += p.batch * p.mom_tiles;
+    blocks += p.batch * p.tiles_r * q.pairs_c;
   }
   L.prefix[plans.size()] = blocks;
   MUON_LAUNCH(KIND_MOMENTUM_NORM, s, launch_momentum_norm(L, dtype, blocks, s));

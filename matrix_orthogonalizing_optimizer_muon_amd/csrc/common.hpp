@@ -144,6 +144,7 @@ struct MomentumGroup {
   int64_t d_stride;   // rp * cp
   double* partials;   // [batch][tiles_per_mat]
   int tiles_r, tiles_c, tiles_per_mat;
+  int pairs_c;        // blocks along a row of tiles: (tiles_c + 1) / 2
   int batch;
   int vec;            // cols % 4 == 0 and bstride % 4 == 0
 };

@@ -6,6 +6,8 @@
 // normalisation follows "Muon and MuonClip: orthogonalised updates for LLM
 // training", Newton-Schulz subsection (X_0 = G / ||G||_F); the parameter write
 // follows "MuonClip", section 03 (W_t = W_{t-1} - lr (scale O_t + wd W_{t-1})).
+#include <utility>
+
 #include "common.hpp"
 
 namespace muon {
@@ -21,24 +23,31 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// One block = one 64 x 64 tile of one matrix in its original layout,
-// covering the zero-padded extent so that every byte of the padded
-// Newton-Schulz inputs is written.  Writes M (in place), U rounded to bf16
-// in its own layout (D1) and transposed (D2), and the tile's sum of u^2.
+// One block = two horizontally adjacent 64 x 64 tiles of one matrix in its
+// original layout (one at the end of an odd row of tiles), covering the
+// zero-padded extent so that every byte of the padded Newton-Schulz inputs is
+// written.  Writes M (in place), U rounded to bf16 in its own layout (D1) and
+// transposed (D2), and each tile's sum of u^2.  When both tiles lie inside
+// the matrix, all of their loads are issued first: each row of the pair is
+// one contiguous 256-byte (G) and 512-byte (M) run.  Against one 64 x 64 tile
+// per block: 5.51-5.57 -> 6.04-6.06 TB/s for the pass on the MuonClip layer
+// (A/B on one box).
 template <typename GT>
 __global__ __launch_bounds__(256) void momentum_norm_kernel(MomentumLaunch L) {
-  __shared__ __attribute__((aligned(16))) bf16_t tr[kTile * kTrPitch];
-  __shared__ double wsum[4];
+  __shared__ __attribute__((aligned(16))) bf16_t tr[2][kTile * kTrPitch];
+  __shared__ double wsum[2][4];
 
   int blk = blockIdx.x;
   int gi = 0;
   while (gi + 1 < L.ngroups && blk >= L.prefix[gi + 1]) ++gi;
   const MomentumGroup& g = L.g[gi];
   const int local = blk - L.prefix[gi];
-  const int mat = local / g.tiles_per_mat;
-  const int t = local - mat * g.tiles_per_mat;
-  const int tr_row = t / g.tiles_c, tr_col = t - tr_row * g.tiles_c;
-  const int i0 = tr_row * kTile, j0 = tr_col * kTile;
+  const int per_mat = g.tiles_r * g.pairs_c;
+  const int mat = local / per_mat;
+  const int t = local - mat * per_mat;
+  const int tr_row = t / g.pairs_c, tc0 = 2 * (t - tr_row * g.pairs_c);
+  const int ntile = min(2, g.tiles_c - tc0);
+  const int i0 = tr_row * kTile;
 
   const GT* G = static_cast<const GT*>(g.G) + mat * g.bstride;
   float* M = g.M ? g.M + mat * g.bstride : nullptr;
@@ -49,75 +58,88 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(MomentumLaunch L) {
   const int c0 = (tid & 15) * 4;
   const int rsub = tid >> 4;
   const float mu = L.mu;
-  double ss = 0.0;
+  double ss[2] = {0.0, 0.0};
 
-  // stores U of one 4-element row segment (own layout + the LDS tile for the
-  // transposed copy) and accumulates its squares.  The own-layout copy is
-  // stored nontemporally: 5.42 -> 5.58 TB/s for the pass on the MuonClip
-  // layer (three tall matrices, one wide); nontemporal stores of the
-  // transposed copy (its 16-byte rows written from LDS) cost 10%.
-  auto emit = [&](int r, const float (&u)[4]) {
+  // stores U of one 4-element row segment of tile h (own layout + the LDS
+  // tile for the transposed copy) and accumulates its squares.  The
+  // own-layout copy is stored nontemporally: 5.42 -> 5.58 TB/s for the pass
+  // on the MuonClip layer (three tall matrices, one wide); nontemporal stores
+  // of the transposed copy (its 16-byte rows written from LDS) cost 10%.
+  auto emit = [&](int h, int r, const float (&u)[4]) {
+    const int j0 = (tc0 + h) * kTile;
     bf16_t ub[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      ss += static_cast<double>(u[q]) * static_cast<double>(u[q]);
+      ss[h] += static_cast<double>(u[q]) * static_cast<double>(u[q]);
       ub[q] = f32_to_bf16(u[q]);
-      tr[(c0 + q) * kTrPitch + r] = ub[q];
+      tr[h][(c0 + q) * kTrPitch + r] = ub[q];
     }
     uint2 packed;
     packed.x = static_cast<uint32_t>(ub[0]) | (static_cast<uint32_t>(ub[1]) << 16);
     packed.y = static_cast<uint32_t>(ub[2]) | (static_cast<uint32_t>(ub[3]) << 16);
     __builtin_nontemporal_store(u32x2_t{packed.x, packed.y}, reinterpret_cast<u32x2_t*>(D1 + static_cast<int64_t>(i0 + r) * g.cp + j0 + c0));
   };
-
-  const bool interior = g.vec && (i0 + kTile <= g.rows) && (j0 + kTile <= g.cols);
-  if (interior) {
-    // whole tile inside the matrix: issue every load first (16 loads per
-    // thread in flight), then compute and store.  G and M are read once per
-    // step: nontemporal loads (M is also written back nontemporally) measured
-    // 5.1 -> 5.4 TB/s for this pass
-    float gv[4][4], mv[4][4];
+  auto inside = [&](int h) {
+    return h < ntile && g.vec && (i0 + kTile <= g.rows) && ((tc0 + h + 1) * kTile <= g.cols);
+  };
+  // Tiles wholly inside the matrix: every load first (16 per tile and thread
+  // in flight), then compute and store.  G and M are read once per step:
+  // nontemporal loads (M is also written back nontemporally) measured 5.1 ->
+  // 5.4 TB/s for this pass.
+  // (HM: momentum present; a compile-time choice, so that no branch separates
+  // the loads and each wave has all of them in flight)
+  auto interior = [&](auto nt, int h0, auto hm) {
+    constexpr int NT = decltype(nt)::value;   // tiles handled together, from tile h0
+    constexpr bool HM = decltype(hm)::value;
+    float gv[NT][4][4], mv[NT][4][4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int64_t e = static_cast<int64_t>(i0 + rsub + 16 * p) * g.cols + j0 + c0;
-      if constexpr (sizeof(GT) == 2) {
-        const u32x2_t rawv = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(G + e));
-        const uint2 raw = make_uint2(rawv[0], rawv[1]);
-        gv[p][0] = bf16_to_f32(raw.x & 0xffff);
-        gv[p][1] = bf16_to_f32(raw.x >> 16);
-        gv[p][2] = bf16_to_f32(raw.y & 0xffff);
-        gv[p][3] = bf16_to_f32(raw.y >> 16);
-      } else {
-        const float4 raw = *reinterpret_cast<const float4*>(G + e);
-        gv[p][0] = raw.x; gv[p][1] = raw.y; gv[p][2] = raw.z; gv[p][3] = raw.w;
-      }
-      if (M) {
-        const f32x4_t m4v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(M + e));
-        const float4 m4 = make_float4(m4v[0], m4v[1], m4v[2], m4v[3]);
-        mv[p][0] = m4.x; mv[p][1] = m4.y; mv[p][2] = m4.z; mv[p][3] = m4.w;
-      }
-    }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = rsub + 16 * p;
-      float u[4];
-      if (M) {
-        float mn[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          mn[q] = fmaf(mu, mv[p][q], gv[p][q]);
-          u[q] = L.nesterov ? fmaf(mu, mn[q], gv[p][q]) : mn[q];
+      for (int hh = 0; hh < NT; ++hh) {
+        const int64_t e = static_cast<int64_t>(i0 + rsub + 16 * p) * g.cols + (tc0 + h0 + hh) * kTile + c0;
+        if constexpr (sizeof(GT) == 2) {
+          const u32x2_t rawv = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(G + e));
+          gv[hh][p][0] = bf16_to_f32(rawv[0] & 0xffff);
+          gv[hh][p][1] = bf16_to_f32(rawv[0] >> 16);
+          gv[hh][p][2] = bf16_to_f32(rawv[1] & 0xffff);
+          gv[hh][p][3] = bf16_to_f32(rawv[1] >> 16);
+        } else {
+          const float4 raw = *reinterpret_cast<const float4*>(G + e);
+          gv[hh][p][0] = raw.x; gv[hh][p][1] = raw.y; gv[hh][p][2] = raw.z; gv[hh][p][3] = raw.w;
         }
-        const int64_t e = static_cast<int64_t>(i0 + r) * g.cols + j0 + c0;
-        f32x4_t mo = {mn[0], mn[1], mn[2], mn[3]};
-        __builtin_nontemporal_store(mo, reinterpret_cast<f32x4_t*>(M + e));
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) u[q] = gv[p][q];
+        if constexpr (HM) {
+          const f32x4_t m4v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(M + e));
+          mv[hh][p][0] = m4v[0]; mv[hh][p][1] = m4v[1]; mv[hh][p][2] = m4v[2]; mv[hh][p][3] = m4v[3];
+        }
       }
-      emit(r, u);
     }
-  } else {
+#pragma unroll
+    for (int hh = 0; hh < NT; ++hh) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = rsub + 16 * p;
+        float u[4];
+        if constexpr (HM) {
+          float mn[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            mn[q] = fmaf(mu, mv[hh][p][q], gv[hh][p][q]);
+            u[q] = L.nesterov ? fmaf(mu, mn[q], gv[hh][p][q]) : mn[q];
+          }
+          const int64_t e = static_cast<int64_t>(i0 + r) * g.cols + (tc0 + h0 + hh) * kTile + c0;
+          f32x4_t mo = {mn[0], mn[1], mn[2], mn[3]};
+          __builtin_nontemporal_store(mo, reinterpret_cast<f32x4_t*>(M + e));
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) u[q] = gv[hh][p][q];
+        }
+        emit(h0 + hh, r, u);
+      }
+    }
+  };
+  // a tile crossing the matrix edge (zero beyond it), one element at a time
+  auto edge = [&](int h) {
+    const int j0 = (tc0 + h) * kTile;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int r = rsub + 16 * p;
@@ -141,30 +163,44 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(MomentumLaunch L) {
           }
         }
       }
-      emit(r, u);
+      emit(h, r, u);
+    }
+  };
+  using Pair = std::integral_constant<int, 2>;
+  using Single = std::integral_constant<int, 1>;
+  if (inside(0) && inside(1)) {
+    if (M) interior(Pair{}, 0, std::true_type{});
+    else interior(Pair{}, 0, std::false_type{});
+  } else {
+    for (int h = 0; h < ntile; ++h) {
+      if (!inside(h)) edge(h);
+      else if (M) interior(Single{}, h, std::true_type{});
+      else interior(Single{}, h, std::false_type{});
     }
   }
 
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  for (int h = 0; h < 2; ++h) {
+    const double w = wave_sum(ss[h]);
+    if ((tid & 63) == 0) wsum[h][tid >> 6] = w;
+  }
   __syncthreads();
 
-  // Transposed tile: row jj of D2 (original column j0 + jj), 16 consecutive
+  // Transposed tiles: row jj of D2 (original column j0 + jj), 16 consecutive
   // original rows per thread.
-  {
+  for (int h = 0; h < ntile; ++h) {
     const int jj = tid >> 2;
     const int ii = (tid & 3) * 16;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tr + jj * kTrPitch + ii);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tr[h] + jj * kTrPitch + ii);
     uint32_t w[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) w[q] = src[q];
-    bf16_t* dst = D2 + static_cast<int64_t>(j0 + jj) * g.rp + i0 + ii;
+    bf16_t* dst = D2 + static_cast<int64_t>((tc0 + h) * kTile + jj) * g.rp + i0 + ii;
     reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
     reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
-  if (tid == 0) {
-    g.partials[static_cast<int64_t>(mat) * g.tiles_per_mat + t] =
-        ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  if (tid < ntile) {
+    g.partials[static_cast<int64_t>(mat) * g.tiles_per_mat + tr_row * g.tiles_c + tc0 + tid] =
+        ((wsum[tid][0] + wsum[tid][1]) + wsum[tid][2]) + wsum[tid][3];
   }
 }
 
