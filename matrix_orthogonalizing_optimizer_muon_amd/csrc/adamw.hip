@@ -4,7 +4,7 @@
 //   m <- b1 m + (1 - b1) g,  v <- b2 v + (1 - b2) g^2,
 //   p <- p (1 - lr wd) - lr (m c1) / (sqrt(v c2) + eps),  c = 1 / (1 - b^t).
 // One HBM pass over many tensors per launch (a block finds its tensor in the
-// block prefix table), 8 elements per thread, fp32 math, one rounding of p.
+// block prefix table), 16 elements per thread, fp32 math, one rounding of p.
 #include "common.hpp"
 
 namespace muon {
@@ -18,85 +18,99 @@ __device__ __forceinline__ void adamw_one(float& p, float g, float& m, float& v,
   p = fmaf(-A.lr, (m * A.c1) / denom, p * A.decay);
 }
 
+// One block = kSpan consecutive elements of one tensor; thread t takes the
+// 4-element groups at t*4 + c*1024 (c = 0..3), so each load instruction of a
+// wave covers one contiguous run (1 KB of m or v) and each thread has all 16
+// of its loads in flight before any arithmetic.
+constexpr int kChunks = 4;
+constexpr int kSpan = 256 * 4 * kChunks;
+
+// Every byte is read once and written once per step: nontemporal loads and
+// stores (6.01-6.05 -> 6.36 TB/s on 235M bf16 parameters, A/B on one box;
+// the coalesced layout alone gave 1%).
+template <typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 template <typename PT>
 __global__ __launch_bounds__(256) void adamw_kernel(AdamWLaunch A) {
   const int b = blockIdx.x;
   int t = 0;
   while (t + 1 < A.ntensors && b >= A.blk_start[t + 1]) ++t;
   const AdamWTensor& T = A.t[t];
-  const int64_t e0 = (static_cast<int64_t>(b - A.blk_start[t]) * 256 + threadIdx.x) * 8;
-  if (e0 >= T.n) return;
+  const int64_t base = static_cast<int64_t>(b - A.blk_start[t]) * kSpan;
   PT* P = static_cast<PT*>(T.p);
   const PT* G = static_cast<const PT*>(T.g);
-  if (T.vec && e0 + 7 < T.n) {
-    float p[8], g[8], m[8], v[8];
-    const f32x4_t* m4 = reinterpret_cast<const f32x4_t*>(T.m + e0);
-    const f32x4_t* v4 = reinterpret_cast<const f32x4_t*>(T.v + e0);
-    const f32x4_t ma = m4[0], mb = m4[1], va = v4[0], vb = v4[1];
-    if constexpr (sizeof(PT) == 2) {
-      const u32x4_t pw = *reinterpret_cast<const u32x4_t*>(P + e0);
-      const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(G + e0);
-      static_for<4>([&](auto q) {
-        constexpr int Q = decltype(q)::value;
-        p[2 * Q] = bf16_to_f32(pw[Q] & 0xffff);
-        p[2 * Q + 1] = bf16_to_f32(pw[Q] >> 16);
-        g[2 * Q] = bf16_to_f32(gw[Q] & 0xffff);
-        g[2 * Q + 1] = bf16_to_f32(gw[Q] >> 16);
-      });
-    } else {
-      const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(P + e0);
-      const f32x4_t* g4 = reinterpret_cast<const f32x4_t*>(G + e0);
-      const f32x4_t pa = p4[0], pb = p4[1], ga = g4[0], gb = g4[1];
-      static_for<4>([&](auto q) {
-        constexpr int Q = decltype(q)::value;
-        p[Q] = pa[Q]; p[Q + 4] = pb[Q];
-        g[Q] = ga[Q]; g[Q + 4] = gb[Q];
-      });
-    }
-    static_for<4>([&](auto q) {
-      constexpr int Q = decltype(q)::value;
-      m[Q] = ma[Q]; m[Q + 4] = mb[Q];
-      v[Q] = va[Q]; v[Q + 4] = vb[Q];
-    });
-    static_for<8>([&](auto q) {
-      constexpr int Q = decltype(q)::value;
-      adamw_one(p[Q], g[Q], m[Q], v[Q], A);
-    });
-    f32x4_t* mo = reinterpret_cast<f32x4_t*>(T.m + e0);
-    f32x4_t* vo = reinterpret_cast<f32x4_t*>(T.v + e0);
-    mo[0] = f32x4_t{m[0], m[1], m[2], m[3]};
-    mo[1] = f32x4_t{m[4], m[5], m[6], m[7]};
-    vo[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-    vo[1] = f32x4_t{v[4], v[5], v[6], v[7]};
-    if constexpr (sizeof(PT) == 2) {
-      u32x4_t pw;
-      static_for<4>([&](auto q) {
-        constexpr int Q = decltype(q)::value;
-        pw[Q] = pack2_bf16(p[2 * Q], p[2 * Q + 1]);
-      });
-      *reinterpret_cast<u32x4_t*>(P + e0) = pw;
-    } else {
-      f32x4_t* p4 = reinterpret_cast<f32x4_t*>(P + e0);
-      p4[0] = f32x4_t{p[0], p[1], p[2], p[3]};
-      p4[1] = f32x4_t{p[4], p[5], p[6], p[7]};
-    }
-  } else {
-    for (int q = 0; q < 8 && e0 + q < T.n; ++q) {
-      const int64_t e = e0 + q;
-      float p, g;
+  const int tid = threadIdx.x;
+  if (T.vec && base + kSpan <= T.n) {
+    float p[kChunks][4], g[kChunks][4];
+    f32x4_t m[kChunks], v[kChunks];
+    static_for<kChunks>([&](auto c) {
+      constexpr int C = decltype(c)::value;
+      const int64_t e = base + C * 1024 + tid * 4;
+      m[C] = ld(reinterpret_cast<const f32x4_t*>(T.m + e));
+      v[C] = ld(reinterpret_cast<const f32x4_t*>(T.v + e));
       if constexpr (sizeof(PT) == 2) {
-        p = bf16_to_f32(reinterpret_cast<const bf16_t*>(P)[e]);
-        g = bf16_to_f32(reinterpret_cast<const bf16_t*>(G)[e]);
+        const u32x2_t pw = ld(reinterpret_cast<const u32x2_t*>(P + e));
+        const u32x2_t gw = ld(reinterpret_cast<const u32x2_t*>(G + e));
+        p[C][0] = bf16_to_f32(pw[0] & 0xffff); p[C][1] = bf16_to_f32(pw[0] >> 16);
+        p[C][2] = bf16_to_f32(pw[1] & 0xffff); p[C][3] = bf16_to_f32(pw[1] >> 16);
+        g[C][0] = bf16_to_f32(gw[0] & 0xffff); g[C][1] = bf16_to_f32(gw[0] >> 16);
+        g[C][2] = bf16_to_f32(gw[1] & 0xffff); g[C][3] = bf16_to_f32(gw[1] >> 16);
       } else {
-        p = P[e];
-        g = G[e];
+        const f32x4_t pw = ld(reinterpret_cast<const f32x4_t*>(P + e));
+        const f32x4_t gw = ld(reinterpret_cast<const f32x4_t*>(G + e));
+        static_for<4>([&](auto q) {
+          constexpr int Q = decltype(q)::value;
+          p[C][Q] = pw[Q];
+          g[C][Q] = gw[Q];
+        });
       }
-      float m = T.m[e], v = T.v[e];
-      adamw_one(p, g, m, v, A);
-      T.m[e] = m;
-      T.v[e] = v;
-      if constexpr (sizeof(PT) == 2) reinterpret_cast<bf16_t*>(P)[e] = f32_to_bf16(p);
-      else P[e] = p;
+    });
+    static_for<kChunks>([&](auto c) {
+      constexpr int C = decltype(c)::value;
+      const int64_t e = base + C * 1024 + tid * 4;
+      float mm[4], vv[4];
+      static_for<4>([&](auto q) {
+        constexpr int Q = decltype(q)::value;
+        mm[Q] = m[C][Q];
+        vv[Q] = v[C][Q];
+        adamw_one(p[C][Q], g[C][Q], mm[Q], vv[Q], A);
+      });
+      st(reinterpret_cast<f32x4_t*>(T.m + e), f32x4_t{mm[0], mm[1], mm[2], mm[3]});
+      st(reinterpret_cast<f32x4_t*>(T.v + e), f32x4_t{vv[0], vv[1], vv[2], vv[3]});
+      if constexpr (sizeof(PT) == 2) {
+        st(reinterpret_cast<u32x2_t*>(P + e), u32x2_t{pack2_bf16(p[C][0], p[C][1]), pack2_bf16(p[C][2], p[C][3])});
+      } else {
+        st(reinterpret_cast<f32x4_t*>(P + e), f32x4_t{p[C][0], p[C][1], p[C][2], p[C][3]});
+      }
+    });
+  } else {
+    // the tensor's last, partial block (or unaligned tensors): one element at a time
+    for (int c = 0; c < kChunks; ++c) {
+      for (int q = 0; q < 4; ++q) {
+        const int64_t e = base + c * 1024 + tid * 4 + q;
+        if (e >= T.n) continue;
+        float p, g;
+        if constexpr (sizeof(PT) == 2) {
+          p = bf16_to_f32(reinterpret_cast<const bf16_t*>(P)[e]);
+          g = bf16_to_f32(reinterpret_cast<const bf16_t*>(G)[e]);
+        } else {
+          p = P[e];
+          g = G[e];
+        }
+        float m = T.m[e], v = T.v[e];
+        adamw_one(p, g, m, v, A);
+        T.m[e] = m;
+        T.v[e] = v;
+        if constexpr (sizeof(PT) == 2) reinterpret_cast<bf16_t*>(P)[e] = f32_to_bf16(p);
+        else P[e] = p;
+      }
     }
   }
 }

@@ -665,7 +665,7 @@ int adamw_step(const adamw_tensor_t* tensors, int n_tensors, int dtype, const ad
     for (; i < n_tensors && A.ntensors < kAdamWMaxTensors; ++i) {
       const adamw_tensor_t& t = tensors[i];
       if (t.numel == 0) continue;
-      const int64_t nb = (t.numel + 2047) / 2048;
+      const int64_t nb = (t.numel + 4095) / 4096;   // 4096 elements per block
       if (A.ntensors > 0 && blocks + nb > (int64_t(1) << 30)) break;
       AdamWTensor& T = A.t[A.ntensors];
       T.p = t.param;
