@@ -569,7 +569,7 @@ int ns_orthogonalize(const void* in, int in_dtype, uint16_t* out, int batch, int
 
 size_t qkclip_rowmax_workspace_size(int B, int T, int H) {
   if (B < 1 || T < 1 || H < 1) return 0;
-  const int nqb = (T + 511) / 512;
+  const int nqb = (T + 255) / 256;   // query blocks of the row-max kernel
   return align_up(static_cast<size_t>(B) * H * nqb * sizeof(float));
 }
 
@@ -580,7 +580,7 @@ int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int
   if (d_head != 64 && d_head != 128 && d_head != 256) return MUON_ERR_UNSUPPORTED;
   if (!aligned(Q, 16) || !aligned(K, 16)) return MUON_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * T * H * d_head > (int64_t(1) << 40)) return MUON_ERR_INVALID_ARG;
-  const int nqb = (T + 511) / 512;
+  const int nqb = (T + 255) / 256;   // query blocks of the row-max kernel
   if (static_cast<int64_t>(B) * H * nqb > (int64_t(1) << 31) - 1) return MUON_ERR_INVALID_ARG;
   const size_t need = qkclip_rowmax_workspace_size(B, T, H);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return MUON_ERR_WORKSPACE;

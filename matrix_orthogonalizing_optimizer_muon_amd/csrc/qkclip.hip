@@ -9,7 +9,7 @@
 // balanced rescale; "About Muon: Muon At Scale", "When Softmax Collapses").
 //
 // The statistic is a causal Q K^T contraction reduced by max, so it runs as
-// a flash-style MFMA loop: one block per (batch row, head, 512 queries), the
+// a flash-style MFMA loop: one block per (batch row, head, 256 queries), the
 // queries' fragments held in registers, 64-key blocks (128 for d = 64)
 // staged through LDS, the logits never stored.  Maxima are reduced across the wavefront with
 // cross-lane max, across the block through LDS, and across blocks by a
@@ -22,8 +22,9 @@ namespace muon {
 
 namespace {
 
-constexpr int kQB = 512;   // queries per block (8 waves x 64)
-constexpr int kThreads = 512;
+constexpr int kQB = 256;   // queries per block (4 waves x 64)
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -31,8 +32,12 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// One block = 512 consecutive queries of one (batch row, head); 8 waves of
-// 64 query rows, two per SIMD.  The queries' fragments stay in registers for
+// One block = 256 consecutive queries of one (batch row, head); 4 waves of
+// 64 query rows, one per SIMD, and two blocks per CU: their barriers are
+// independent, so one block's MFMAs run while the other stages keys or
+// waits (8-wave blocks of 512 queries, two waves per SIMD in one block, took
+// 16% longer: both waves of a SIMD reached each barrier together and left its
+// MFMA pipe idle while the keys were staged).  The queries' fragments stay in registers for
 // the whole key sweep; KB keys at a time are staged through double-buffered
 // LDS (registers one stage ahead, barrier without the workgroup fence so the
 // prefetch stays in flight).  Logits are reduced by max in registers; only
@@ -50,8 +55,8 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   constexpr int NCH = KB / RPP;               // chunks per thread per stage
   static_assert(KB % RPP == 0, "staging map must cover the stage exactly");
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][KB * PITCH];
-  __shared__ float wmax[8];
-  __shared__ int wnan[8];
+  __shared__ float wmax[kWaves];
+  __shared__ int wnan[kWaves];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / nqb;
@@ -184,7 +189,7 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   if (tid == 0) {
     float r = wmax[0];
     int nan = wnan[0];
-    for (int w = 1; w < 8; ++w) {
+    for (int w = 1; w < kWaves; ++w) {
       r = fmaxf(r, wmax[w]);
       nan |= wnan[w];
     }
