@@ -293,24 +293,49 @@ void ns_gemm_kernel(GemmLaunch L) {
   gload(1);
   barrier();
   read_frags(0, 0, std::integral_constant<int, 0>{});
-  for (int kt = 0; kt < KT; ++kt) {
+  // E rows 0-127 of whole 256-tiles (the epilogue's a X or b A term), 8
+  // chunks per thread in the copy-in map, fetched during the last K slice
+  constexpr bool PRE = (TM == 256 && TN == 256);
+  constexpr int EPT = TM + 8;                  // staged Ct / Et tile row pitch, TN rows
+  static_assert(!PRE || NCP + NCQ == 128 * (TM / 8) / NT, "an E half must fill the staging registers");
+  const bool pre = PRE && p.Et != nullptr;
+  auto gload_e0 = [&]() {
+    const bf16_t* E = p.Et + mat * p.sEt + static_cast<int64_t>(col0) * p.lde + row0;
+    const int r = tid / (TM / 8), cc = (tid % (TM / 8)) * 8;
+    static_for<NCP>([&](auto c) {
+      rP[c] = *reinterpret_cast<const u32x4_t*>(E + static_cast<int64_t>(r + (NT / (TM / 8)) * c) * p.lde + cc);
+    });
+    static_for<NCQ>([&](auto c) {
+      rQ[c] = *reinterpret_cast<const u32x4_t*>(E + static_cast<int64_t>(r + (NT / (TM / 8)) * (NCP + c)) * p.lde + cc);
+    });
+  };
+  // one K slice; the last one stages nothing (its prefetch slot fetches E)
+  auto kslice = [&](int kt, auto last) {
+    constexpr bool LAST = decltype(last)::value;
     const int cur = kt & 1;
     static_for<S - 1>([&](auto s) {
       constexpr int SS = decltype(s)::value;
       read_frags(cur, SS + 1, std::integral_constant<int, (SS + 1) & 1>{});
-      if constexpr (SS == S - 2) {
+      if constexpr (SS == S - 2 && !LAST) {
         // stage slice kt+1 (loaded one iteration ago), then prefetch kt+2
         sstore(cur ^ 1);
         gload(kt + 2);
       }
+      if constexpr (SS == S - 2 && LAST) {
+        if (pre) gload_e0();
+      }
       mfmas(std::integral_constant<int, SS & 1>{});
-      pattern(SS == S - 2 ? NCP + NCQ : 0, SS == S - 2 ? NCP + NCQ : 0);
+      pattern(SS == S - 2 && !LAST ? NCP + NCQ : 0, SS == S - 2 && !LAST ? NCP + NCQ : 0);
     });
-    barrier();
-    read_frags(cur ^ 1, 0, std::integral_constant<int, 0>{});
+    if constexpr (!LAST) {
+      barrier();
+      read_frags(cur ^ 1, 0, std::integral_constant<int, 0>{});
+    }
     mfmas(std::integral_constant<int, (S - 1) & 1>{});
     pattern(0, 0);
-  }
+  };
+  for (int kt = 0; kt < KT - 1; ++kt) kslice(kt, std::false_type{});
+  kslice(KT - 1, std::true_type{});
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue.  Element e of acc[a][b] holds C[i][j] with
@@ -325,7 +350,6 @@ void ns_gemm_kernel(GemmLaunch L) {
     sc = (p.alpha_pow == 2) ? al * al : al;
   }
   constexpr int EPC = TN + 8;                  // staged C tile row pitch (bf16), TM rows
-  constexpr int EPT = TM + 8;                  // staged Ct / Et tile row pitch, TN rows
   static_assert(TM * EPC <= 2 * (TM + TN) * kPitch && TN * EPT <= 2 * (TM + TN) * kPitch,
                 "staged tile must fit the LDS buffer");
   EpiArgs e;
@@ -341,7 +365,19 @@ void ns_gemm_kernel(GemmLaunch L) {
   bf16_t* C = p.C ? p.C + mat * p.sC : nullptr;
   bf16_t* Ct = (p.Ct && (!p.sym || ti != tj)) ? p.Ct + mat * p.sCt : nullptr;
   lds_barrier();                // every wave is done with the K slices
-  if (p.Et) {
+  if (pre) {
+    // E rows 0-127 from the registers, rows 128-255 from memory
+    const int r = tid / (TM / 8), cc = (tid % (TM / 8)) * 8;
+    static_for<NCP>([&](auto c) {
+      *reinterpret_cast<u32x4_t*>(smem + (r + (NT / (TM / 8)) * c) * EPT + cc) = rP[c];
+    });
+    static_for<NCQ>([&](auto c) {
+      *reinterpret_cast<u32x4_t*>(smem + (r + (NT / (TM / 8)) * (NCP + c)) * EPT + cc) = rQ[c];
+    });
+    copy_in<TN / 2, TM, EPT, NT>(smem + (TN / 2) * EPT, p.Et + mat * p.sEt, p.lde, col0 + TN / 2, row0, tid);
+    lds_barrier();
+    e.Et = smem;
+  } else if (p.Et) {
     // E[j][i] block (the transposed layout of this output block), coalesced into LDS
     copy_in<TN, TM, EPT, NT>(smem, p.Et + mat * p.sEt, p.lde, col0, row0, tid);
     lds_barrier();
