@@ -45,6 +45,7 @@ struct EpiArgs {
   int lde;
   int gi0, gj0;       // this lane's first row / column in the matrix (block (0, 0))
   int li0, lj0;       // the same inside the tile
+  int ljE;            // this lane's first row of the staged E tile (Et)
 };
 
 template <int A, int B, int Qd>
@@ -58,7 +59,7 @@ __device__ __forceinline__ u32x2_t epi_quad(const f32x16_t& acc, const EpiArgs& 
   });
   if (e.Et) {
     // the Et tile staged in LDS, layout [j][i]
-    const u32x2_t ev = *reinterpret_cast<const u32x2_t*>(e.Et + (e.lj0 + 32 * B) * e.lde + e.li0 + 32 * A + 8 * Qd);
+    const u32x2_t ev = *reinterpret_cast<const u32x2_t*>(e.Et + (e.ljE + 32 * B) * e.lde + e.li0 + 32 * A + 8 * Qd);
     v[0] = fmaf(e.ce, bf16_to_f32(ev[0] & 0xffff), v[0]);
     v[1] = fmaf(e.ce, bf16_to_f32(ev[0] >> 16), v[1]);
     v[2] = fmaf(e.ce, bf16_to_f32(ev[1] & 0xffff), v[2]);
@@ -133,8 +134,8 @@ void ns_gemm_kernel(GemmLaunch L) {
 
   // two stages of the P and Q slices; the epilogue reuses the whole buffer
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (TM + TN) * kPitch];
-  auto sP = [&](int buf) { return smem + buf * TM * kPitch; };
-  auto sQ = [&](int buf) { return smem + 2 * TM * kPitch + buf * TN * kPitch; };
+  auto sP = [&](int buf) { return smem + buf * (TM + TN) * kPitch; };   // a stage: P then Q slice
+  auto sQ = [&](int buf) { return smem + buf * (TM + TN) * kPitch + TM * kPitch; };
 
   // ---- block -> (problem, matrix, tile, column slice)
   int vb, slice = 0;
@@ -293,15 +294,20 @@ void ns_gemm_kernel(GemmLaunch L) {
   gload(1);
   barrier();
   read_frags(0, 0, std::integral_constant<int, 0>{});
-  // E rows 0-127 of whole 256-tiles (the epilogue's a X or b A term), 8
-  // chunks per thread in the copy-in map, fetched during the last K slice
+  // The E tile of whole 256-tiles (the epilogue's a X or b A term) rides in
+  // the last two K slices' prefetch slots, which would otherwise repeat the
+  // last slice: rows 128-255 during the second-to-last slice (then staged in
+  // the spare LDS stage during the last), rows 0-127 during the last (staged
+  // by the epilogue).  8 chunks per thread in the copy-in map per half.
   constexpr bool PRE = (TM == 256 && TN == 256);
   constexpr int EPT = TM + 8;                  // staged Ct / Et tile row pitch, TN rows
-  static_assert(!PRE || NCP + NCQ == 128 * (TM / 8) / NT, "an E half must fill the staging registers");
+  static_assert(!PRE || (NCP + NCQ == 128 * (TM / 8) / NT && 128 * EPT <= (TM + TN) * kPitch),
+                "an E half must fill the staging registers and fit one stage");
   const bool pre = PRE && p.Et != nullptr;
-  auto gload_e0 = [&]() {
-    const bf16_t* E = p.Et + mat * p.sEt + static_cast<int64_t>(col0) * p.lde + row0;
-    const int r = tid / (TM / 8), cc = (tid % (TM / 8)) * 8;
+  const int er = tid / (TM / 8), ec = (tid % (TM / 8)) * 8;   // this thread's E chunk
+  auto gload_e = [&](int half) {
+    const bf16_t* E = p.Et + mat * p.sEt + static_cast<int64_t>(col0 + 128 * half) * p.lde + row0;
+    const int r = er, cc = ec;
     static_for<NCP>([&](auto c) {
       rP[c] = *reinterpret_cast<const u32x4_t*>(E + static_cast<int64_t>(r + (NT / (TM / 8)) * c) * p.lde + cc);
     });
@@ -309,33 +315,52 @@ void ns_gemm_kernel(GemmLaunch L) {
       rQ[c] = *reinterpret_cast<const u32x4_t*>(E + static_cast<int64_t>(r + (NT / (TM / 8)) * (NCP + c)) * p.lde + cc);
     });
   };
-  // one K slice; the last one stages nothing (its prefetch slot fetches E)
-  auto kslice = [&](int kt, auto last) {
-    constexpr bool LAST = decltype(last)::value;
+  // an E half in the staging registers, to rows 0-127 of a stage-sized region
+  auto sstore_e = [&](bf16_t* base) {
+    static_for<NCP>([&](auto c) {
+      *reinterpret_cast<u32x4_t*>(base + (er + (NT / (TM / 8)) * c) * EPT + ec) = rP[c];
+    });
+    static_for<NCQ>([&](auto c) {
+      *reinterpret_cast<u32x4_t*>(base + (er + (NT / (TM / 8)) * (NCP + c)) * EPT + ec) = rQ[c];
+    });
+  };
+  // one K slice: MODE 0 stages slice kt + 1 and prefetches kt + 2; MODE 1
+  // (second-to-last) stages the last slice and fetches E rows 128-255;
+  // MODE 2 (last) stages those E rows into the spare stage and fetches rows 0-127
+  auto kslice = [&](int kt, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
     const int cur = kt & 1;
     static_for<S - 1>([&](auto s) {
       constexpr int SS = decltype(s)::value;
       read_frags(cur, SS + 1, std::integral_constant<int, (SS + 1) & 1>{});
-      if constexpr (SS == S - 2 && !LAST) {
+      if constexpr (SS == S - 2 && MODE == 0) {
         // stage slice kt+1 (loaded one iteration ago), then prefetch kt+2
         sstore(cur ^ 1);
         gload(kt + 2);
       }
-      if constexpr (SS == S - 2 && LAST) {
-        if (pre) gload_e0();
+      if constexpr (SS == S - 2 && MODE == 1) {
+        sstore(cur ^ 1);
+        if (pre) gload_e(1);
+      }
+      if constexpr (SS == S - 2 && MODE == 2) {
+        if (pre) {
+          sstore_e(sP(cur ^ 1));
+          gload_e(0);
+        }
       }
       mfmas(std::integral_constant<int, SS & 1>{});
-      pattern(SS == S - 2 && !LAST ? NCP + NCQ : 0, SS == S - 2 && !LAST ? NCP + NCQ : 0);
+      pattern(SS == S - 2 && MODE == 0 ? NCP + NCQ : 0, SS == S - 2 && MODE == 0 ? NCP + NCQ : 0);
     });
-    if constexpr (!LAST) {
+    if constexpr (MODE != 2) {
       barrier();
       read_frags(cur ^ 1, 0, std::integral_constant<int, 0>{});
     }
     mfmas(std::integral_constant<int, (S - 1) & 1>{});
     pattern(0, 0);
   };
-  for (int kt = 0; kt < KT - 1; ++kt) kslice(kt, std::false_type{});
-  kslice(KT - 1, std::true_type{});
+  for (int kt = 0; kt < KT - 2; ++kt) kslice(kt, std::integral_constant<int, 0>{});
+  kslice(KT - 2, std::integral_constant<int, 1>{});
+  kslice(KT - 1, std::integral_constant<int, 2>{});
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue.  Element e of acc[a][b] holds C[i][j] with
@@ -362,21 +387,18 @@ void ns_gemm_kernel(GemmLaunch L) {
   e.gj0 = col0 + wc0 + (lane & 31);
   e.li0 = wr0 + 4 * (lane >> 5);
   e.lj0 = wc0 + (lane & 31);
+  e.ljE = e.lj0;
   bf16_t* C = p.C ? p.C + mat * p.sC : nullptr;
   bf16_t* Ct = (p.Ct && (!p.sym || ti != tj)) ? p.Ct + mat * p.sCt : nullptr;
   lds_barrier();                // every wave is done with the K slices
   if (pre) {
-    // E rows 0-127 from the registers, rows 128-255 from memory
-    const int r = tid / (TM / 8), cc = (tid % (TM / 8)) * 8;
-    static_for<NCP>([&](auto c) {
-      *reinterpret_cast<u32x4_t*>(smem + (r + (NT / (TM / 8)) * c) * EPT + cc) = rP[c];
-    });
-    static_for<NCQ>([&](auto c) {
-      *reinterpret_cast<u32x4_t*>(smem + (r + (NT / (TM / 8)) * (NCP + c)) * EPT + cc) = rQ[c];
-    });
-    copy_in<TN / 2, TM, EPT, NT>(smem + (TN / 2) * EPT, p.Et + mat * p.sEt, p.lde, col0 + TN / 2, row0, tid);
+    // E rows 128-255 wait in the spare stage (KT & 1); rows 0-127, in the
+    // registers, go to the stage the last K slice used
+    sstore_e(sP((KT - 1) & 1));
     lds_barrier();
-    e.Et = smem;
+    const bool hi = wc0 >= 128;
+    e.Et = sP(hi ? KT & 1 : (KT - 1) & 1);
+    e.ljE = hi ? e.lj0 - 128 : e.lj0;
   } else if (p.Et) {
     // E[j][i] block (the transposed layout of this output block), coalesced into LDS
     copy_in<TN, TM, EPT, NT>(smem, p.Et + mat * p.sEt, p.lde, col0, row0, tid);
