@@ -71,12 +71,14 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   const int r0 = qb * kQB + wave * 64;  // first query row of this wave
   const int frow = lane & 31, fk = (lane >> 5) * 8;
 
+  // Rows past T load row T - 1 instead (every load unconditional, so the
+  // compiler can count outstanding loads instead of draining them all before
+  // each LDS store); their logits are masked out below.
   bf16x8_t qf[2][KS];
   static_for<2>([&](auto a) {
-    const int row = r0 + a * 32 + frow;
+    const int row = min(r0 + a * 32 + frow, T - 1);
     static_for<KS>([&](auto s) {
-      if (row < T) qf[a][s] = *reinterpret_cast<const bf16x8_t*>(Qb + row * row_stride + s * 16 + fk);
-      else qf[a][s] = bf16x8_t{};
+      qf[a][s] = *reinterpret_cast<const bf16x8_t*>(Qb + row * row_stride + s * 16 + fk);
     });
   });
 
@@ -92,9 +94,8 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   auto gload = [&](int kb, auto set) {
     constexpr int SET = decltype(set)::value;
     static_for<NCH>([&](auto c) {
-      const int j = kb * KB + lrow + c * RPP;
-      if (j < T) rk[SET][c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + lcol);
-      else rk[SET][c] = u32x4_t{};
+      const int j = min(kb * KB + lrow + c * RPP, T - 1);
+      rk[SET][c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + lcol);
     });
   };
   auto sstore = [&](int buf, auto set) {
@@ -110,10 +111,10 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  // prefetches past the last key block reload the last block into a set
+  // that is never stored, rather than branching around the loads
   gload(0, S0{});
-  if constexpr (NS == 2) {
-    if (nkb > 1) gload(1, S1{});
-  }
+  if constexpr (NS == 2) gload(min(1, nkb - 1), S1{});
   sstore(0, S0{});
   barrier();
   auto body = [&](int kb, auto par) {
@@ -122,7 +123,7 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     constexpr int SS = (NS == 2) ? (P ^ 1) : 0;    // set holding block kb + 1
     const int cur = kb & 1;
     const bool more = kb + 1 < nkb;
-    if (kb + NS < nkb) gload(kb + NS, std::integral_constant<int, LS>{});
+    gload(min(kb + NS, nkb - 1), std::integral_constant<int, LS>{});
     const int c0 = kb * KB;
     const bool any = (r0 < T) && (!causal || c0 <= r0 + 63);
     if (any) {
