@@ -79,8 +79,11 @@ def test_rms_identity_and_level(shape):
     rms = np.sqrt(np.mean(upd ** 2))
     sv = np.linalg.svd(O_, compute_uv=False)
     assert abs(rms - 0.2 * np.sqrt(np.mean(sv ** 2))) < 1e-12
-    # a full-rank Gaussian input lands every normalised singular value above
-    # 0.0015 only loosely, so allow the band the survey of the polynomial gives
+    # 0.2 x the tuned iteration's output band of about 0.68 to 1.2 ("Muon and
+    # MuonClip: orthogonalised updates for LLM training", "Newton-Schulz: an
+    # odd polynomial on singular values"), widened slightly: a full-rank
+    # Gaussian input puts only most of its normalised singular values above
+    # the 0.0015 floor that band assumes
     assert 0.13 <= rms <= 0.25
 
 
