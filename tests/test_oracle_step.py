@@ -126,3 +126,51 @@ def test_bf16_specials():
     assert (b[2] & 0x7F80) == 0x7F80 and (b[2] & 0x7F) != 0
     w = O.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0001], dtype=np.uint16))
     assert list(w) == [1.0, -2.0, 2.0 ** -133]
+
+
+def _closed_form_ns(U, steps=5, abc=(3.4445, -4.7750, 2.0315), eps=1e-7):
+    """Newton-Schulz of U in closed form from NumPy's SVD: the iteration maps
+    each normalised singular value s to the composed odd polynomial p^steps(s)
+    and keeps the singular vectors ("Muon and MuonClip: orthogonalised
+    updates for LLM training", "Newton-Schulz: an odd polynomial on singular
+    values")."""
+    a, b, c = abc
+    Uu, S, Vt = np.linalg.svd(U, full_matrices=False)
+    s = S / (np.linalg.norm(U) + eps)
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return (Uu * s) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(12, 7), (7, 12), (9, 9)])
+def test_lookahead_uses_the_new_momentum(shape):
+    """A warm momentum buffer that is not parallel to the gradient.  "MuonClip",
+    section 02 writes the momentum M_t = mu M_{t-1} + G_t; the lookahead adds
+    mu M_t to the gradient, so Newton-Schulz acts on
+        U = G_t + mu (mu M_{t-1} + G_t) = (1 + mu) G_t + mu^2 M_{t-1}.
+    The oracle's O must equal the SVD closed form of that matrix, and the
+    stored momentum must be mu M_{t-1} + G_t.  Building U from M_{t-1} instead
+    (U = G_t + mu M_{t-1}) moves O far outside the closed form's rounding,
+    which the last assertion checks, so this pin catches that mistake.  A
+    second step repeats the check with the first step's momentum as M_{t-1}."""
+    rng = np.random.default_rng(11)
+    mu = 0.9
+    W = rng.standard_normal(shape) * 0.02
+    M0 = rng.standard_normal(shape) * 3.0
+    G1 = rng.standard_normal(shape)
+    W1, M1, O1 = O.muon_step(W, M0, G1, lr=0.02, momentum=mu, weight_decay=0.1, nesterov=True)
+    assert np.allclose(M1, mu * M0 + G1, rtol=0, atol=1e-14)
+    expect = _closed_form_ns((1 + mu) * G1 + mu * mu * M0)
+    assert np.linalg.norm(O1 - expect) <= 1e-11 * np.linalg.norm(expect)
+    wrong = _closed_form_ns(G1 + mu * M0)
+    assert np.linalg.norm(O1 - wrong) >= 1e-2 * np.linalg.norm(expect)
+    # second step, fresh gradient, warm M1
+    G2 = rng.standard_normal(shape)
+    _, M2, O2 = O.muon_step(W1, M1, G2, lr=0.02, momentum=mu, weight_decay=0.1, nesterov=True)
+    assert np.allclose(M2, mu * M1 + G2, rtol=0, atol=1e-13)
+    expect2 = _closed_form_ns((1 + mu) * G2 + mu * mu * M1)
+    assert np.linalg.norm(O2 - expect2) <= 1e-11 * np.linalg.norm(expect2)
+    # without the lookahead Newton-Schulz acts on the momentum itself
+    _, _, O3 = O.muon_step(W, M0, G1, lr=0.02, momentum=mu, weight_decay=0.1, nesterov=False)
+    expect3 = _closed_form_ns(mu * M0 + G1)
+    assert np.linalg.norm(O3 - expect3) <= 1e-11 * np.linalg.norm(expect3)
