@@ -1,18 +1,22 @@
-"""Benchmark: one MuonClip layer step on one MI355X.
+"""Benchmark: the Muon step of a 24-layer dense decoder on one MI355X.
 
-A step is the whole path on the MuonClip attention layer (hidden 7168,
-64 heads x 128, batch 4 x seq 4096, bf16): the per-head causal max-logit
-statistic on the forward's Q and K, the Muon step (momentum + Nesterov +
-Frobenius pass, 5 quintic Newton-Schulz iterations as bf16 MFMA GEMMs,
-scaled and decayed parameter write) on W_q, W_k, W_v [8192 x 7168] and
-W_o [7168 x 8192], then the per-head W_q / W_k rescale at tau = 100.
+The headline step is the whole Muon path on the decoder's Muon group (hidden
+4096, 32 query / 8 KV heads of 128, FFN 14336; per layer W_q, W_o 4096x4096,
+W_k, W_v 1024x4096, up and gate 14336x4096, down 4096x14336; 168 matrices,
+bf16 params and grads, fp32 momentum): the momentum + Nesterov + Frobenius
+pass, 5 quintic Newton-Schulz iterations as bf16 MFMA GEMMs batched by shape
+class, and the scaled, decayed parameter write.  It is the largest workload
+that fits one GPU.  The MuonClip attention layer (per-head causal max-logit
+statistic on the forward's Q and K, Muon step on W_q, W_k, W_v [8192x7168] and
+W_o [7168x8192], per-head rescale at tau = 100), the hidden-2048 layer, the
+64-expert MoE stack and the single 256x128 fp32 matrix are reported beside it.
 
 Inputs are seeded and synthetic and resident in HBM before timing.  Per-kernel
-times come from HIP events recorded by the library around each launch on the
+times come from HIP events the library records around each launch on the
 benchmark stream.  The CPU baseline times the fp64 oracle on a bounded sample
-of the same workload and extrapolates to one step.
+(one matrix per shape class) and extrapolates to one step.
 
-Prints one JSON line.
+Prints one JSON line on stdout; progress lines go to stderr.
 """
 from __future__ import annotations
 
@@ -27,36 +31,66 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16
-# a register-only MFMA loop measured on the box: 2.11-2.14 PFLOP/s, shader clock
-# 2.07-2.10 GHz under that load
-MFMA_BF16_MEASURED_TFLOPS = 2120.0
 HBM_PEAK_GBS = 8000.0
 MFMA_FP32_PEAK_TFLOPS = 157.3    # dense fp32 MFMA, the spec figure
+NS_KINDS = ("ns_syrk_xxt", "ns_syrk_poly", "ns_gemm_bx")
+SLICE_KINDS = ("ns_syrk_xxt_slices", "ns_syrk_poly_slices")
+THIN_KINDS = ("ns_thin_gram", "ns_thin_poly", "ns_thin_bx")
+HEADLINE_TRAFFIC = os.path.join("profiles", "decoder24_step_hbm_traffic.txt")
+LAYER_TRAFFIC = os.path.join("profiles", "muonclip_layer_step_hbm_traffic.txt")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-other-configs", action="store_true",
-                    help="skip the readings of the 24-layer decoder and the MoE stack")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the decoder step alone (for profiler runs)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time the MuonClip layer step alone (for profiler runs)")
     ap.add_argument("--seed", type=int, default=5000)
     ap.add_argument("--blas-reference", action="store_true",
                     help="time torch.matmul (hipBLASLt) on the full, unsymmetric Newton-Schulz "
-                         "products of the same shapes, for comparison, and exit")
+                         "products of the MuonClip layer's shape, for comparison, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM counters)")
+    ap.add_argument("--summarize-profile", nargs="+", metavar="CSV",
+                    help="print a per-kernel summary of rocprofv3 kernel-trace or counter CSV "
+                         "files and exit (no GPU use)")
     return ap.parse_args()
 
 
-def measured_traffic():
-    """Per-launch HBM bytes from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+def note(msg):
+    """A progress line on stderr (the JSON result alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+
+def ns_flops(m, n):
+    """Algorithmic flops of one Newton-Schulz iteration on a wide m x n matrix
+    with the symmetric products counted once: X X^T (upper triangle incl.
+    diagonal: m(m+1)/2 dots of length n), A A^T (m(m+1)/2 dots of length m),
+    B X (m n dots of length m)."""
+    return {"ns_syrk_xxt": m * (m + 1) * n, "ns_syrk_poly": m * m * (m + 1), "ns_gemm_bx": 2 * m * m * n}
+
+
+def ns_flops_dense(m, n):
+    """The pages' count for one iteration, 2 (2 n m^2 + m^3) ("Muon and
+    MuonClip", Newton-Schulz cost paragraph): every product in full."""
+    return 2 * (2 * n * m * m + m ** 3)
+
+
+def measured_traffic(path):
+    """Per-launch HBM bytes from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary, keyed by kernel; an entry is used only while the hash of its
     kernel source still matches the source the counters were taken on."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "muonclip_layer_step_hbm_traffic.txt")
+    path = os.path.join(ROOT, path)
     if not os.path.exists(path):
         return {}
     data = {}
@@ -74,60 +108,249 @@ def measured_traffic():
     return out
 
 
-def ns_flops(m, n):
-    """Algorithmic flops of one Newton-Schulz iteration on a wide m x n matrix
-    with the symmetric products counted once: X X^T (upper triangle incl.
-    diagonal: m(m+1)/2 dots of length n), A A^T (m(m+1)/2 dots of length m),
-    B X (m n dots of length m)."""
-    return {"ns_syrk_xxt": m * (m + 1) * n, "ns_syrk_poly": m * m * (m + 1), "ns_gemm_bx": 2 * m * m * n}
-
-
-def note(msg):
-    """A progress line on stderr (the JSON result alone goes to stdout)."""
-    print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(the step shards by whole matrices across GPUs, which is not built here)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
-        src.fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
-            dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 3
-        print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 3,
-                          "copy_GBs_read_plus_write": round(2 * src.numel() / ms / 1e6, 1)}))
+        print(json.dumps(copy_calibration(torch)))
         return
-
     if args.blas_reference:
         print(json.dumps(blas_reference(torch)), flush=True)
         return
 
     import matrix_orthogonalizing_optimizer_muon_amd as mm
-    from synthetic import generators as gen
-
     dev = torch.device("cuda:0")
+    seed = args.seed
+
+    if args.layer_only:
+        res = muonclip_layer_reading(mm, torch, dev, seed, args.steps, args.warmup)
+        print(json.dumps(res), flush=True)
+        return
+
+    peak = None if args.headline_only else mfma_peak(mm, torch, dev)
+    if peak:
+        note(f"register-only MFMA loop: {peak['tflops']} TFLOP/s")
+
+    # ---------------- headline: the 24-layer decoder's Muon group
+    head = muon_config_run(mm, torch, dev, seed, 3, args.steps, args.warmup, roofline=True)
+    note("24-layer decoder step timed")
+    out = {
+        "metric": "Muon steps/s + Newton–Schulz TFLOP/s (% bf16 MFMA peak), 1 MI355X",
+        "value": head["steps_per_s"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "ns_steps": 5, "matrices": head["matrices"],
+                   "parallelism": "single GPU"},
+    }
+    for k in ("median_ms_per_step", "ns_tflops", "ns_frac_mfma_peak", "ns_ms_per_step",
+              "ns_tflops_dense_equivalent", "roofline", "hbm_passes", "kernels"):
+        out[k] = head[k]
+    if peak:
+        out["mfma_measured_peak"] = peak
+        out["ns_frac_measured_mfma_peak"] = round(head["ns_tflops"] / peak["tflops"], 4)
+        out["roofline"]["measured_peak"] = peak["tflops"]
+        out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["achieved"] / peak["tflops"], 4)
+    torch.cuda.empty_cache()
+
+    if not args.headline_only:
+        out["muonclip_layer"] = muonclip_layer_reading(mm, torch, dev, seed, args.steps, args.warmup,
+                                                       companions=True)
+        note("MuonClip layer step timed")
+        out["layer_hidden2048"] = muon_config_run(mm, torch, dev, seed, 2, args.steps, args.warmup)
+        note("hidden-2048 layer timed")
+        out["moe_64_experts"] = muon_config_run(mm, torch, dev, seed, 4, args.steps, args.warmup)
+        note("64-expert MoE stack timed")
+        out["single_matrix_256x128"] = small_matrix_reading(mm, torch, dev, seed)
+        note("single 256x128 matrix timed")
+        out["dion_rank128"] = dion_reading(mm, torch, dev, seed)
+        note("Dion step timed")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decoder(seed)
+        note("CPU baseline timed")
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# readings
+# ---------------------------------------------------------------------------
+
+def mfma_peak(mm, torch, dev, iters=20000):
+    """The register-only MFMA loop on every CU (two 256-thread blocks per CU,
+    one wave per SIMD each), timed with events: the sustained bf16 matrix-core
+    rate at the clock the chip holds under that load."""
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * ncu
+    sink = torch.empty(blocks, dtype=torch.float32, device=dev)
+    mm.mfma_probe(blocks, 200, sink)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flop = mm.mfma_probe(blocks, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return {"tflops": round(best, 1), "frac_of_spec": round(best / MFMA_BF16_PEAK_TFLOPS, 4),
+            "probe": f"{blocks} blocks x 4 waves x 4 x {iters} v_mfma_f32_32x32x16_bf16, best of 3"}
+
+
+def make_config_groups(mm, torch, dev, seed, idx):
+    """The groups of one workload drawn on the GPU with its recipe (bf16
+    params and grads, fp32 momentum; grads N(0,1), low-rank-plus-noise, or
+    low-rank-plus-noise with Zipf(1.1) expert magnitudes)."""
+    from synthetic import generators as gen
+    wl = gen.workload(idx)
+    groups = []
+    for gi, gr in enumerate(wl.groups):
+        W = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.02, seed + 100 + gi, dev, torch.bfloat16)
+        if wl.grad_kind == "normal":
+            G = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 1.0, seed + 200 + gi, dev, torch.bfloat16)
+        else:
+            mags = gen.zipf_magnitudes(gen.rng(seed + 7), gr.batch) if wl.grad_kind == "lowrank_zipf" \
+                else [1.0] * gr.batch
+            G = torch.stack([gen.lowrank_torch(gr.rows, gr.cols, seed + 200 + 1000 * gi + b, dev,
+                                               magnitude=float(mags[b])) for b in range(gr.batch)])
+        M = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.5, seed + 300 + gi, dev, torch.float32)
+        groups.append((W, G, M))
+    hp = mm.HParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=True,
+                    ns_steps=wl.ns_steps, ns_coeffs=wl.ns_coeffs, ns_eps=wl.ns_eps, rms_target=wl.rms_target)
+    return wl, groups, hp
+
+
+def timed_steps(mm, torch, step, steps, warmup):
+    """W untimed steps, then exactly K timed steps between two device
+    synchronisations, with an event per step for the median; the library's
+    per-kernel events are recorded meanwhile."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    mm.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for k in range(steps):
+        step()
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = mm.profile_collect()
+    mm.profile_enable(False)
+    per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+    median = per[len(per) // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    return elapsed, median, prof
+
+
+def ns_summary(wl, prof, steps):
+    """Newton-Schulz flops and time per step over the tiled and thin products."""
+    flop = dense = 0.0
+    per_kind = {k: 0.0 for k in NS_KINDS}
+    for gr in wl.groups:
+        m, n = min(gr.rows, gr.cols), max(gr.rows, gr.cols)
+        f = ns_flops(m, n)
+        for k in NS_KINDS:
+            per_kind[k] += gr.batch * wl.ns_steps * f[k]
+        flop += gr.batch * wl.ns_steps * sum(f.values())
+        dense += gr.batch * wl.ns_steps * ns_flops_dense(m, n)
+    ns_ms = sum(prof[k][0] for k in NS_KINDS + SLICE_KINDS + THIN_KINDS if k in prof) / steps
+    return flop, dense, per_kind, ns_ms
+
+
+def muon_config_run(mm, torch, dev, seed, idx, steps, warmup, roofline=False):
+    """The Muon step alone on one workload, all its groups in one call."""
+    wl, groups, hp = make_config_groups(mm, torch, dev, seed, idx)
+    ws = torch.empty(mm.workspace_size(groups), dtype=torch.uint8, device=dev)
+    elapsed, median, prof = timed_steps(mm, torch, lambda: mm.muon_step(groups, hp, workspace=ws), steps, warmup)
+    flop, dense, per_kind, ns_ms = ns_summary(wl, prof, steps)
+    nmat = sum(g.batch for g in wl.groups)
+    res = {"workload": wl.name + ": " + ", ".join(f"{g.batch} x {g.rows}x{g.cols}" for g in wl.groups),
+           "matrices": nmat, "steps": steps, "warmup": warmup,
+           "steps_per_s": round(steps / elapsed, 3), "ms_per_step": round(1e3 * elapsed / steps, 3),
+           "median_ms_per_step": round(median, 3),
+           "ns_ms_per_step": round(ns_ms, 3),
+           "ns_tflops": round(flop / (ns_ms * 1e-3) / 1e12, 1),
+           "ns_frac_mfma_peak": round(flop / (ns_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "ns_tflops_dense_equivalent": round(dense / (ns_ms * 1e-3) / 1e12, 1),
+           "kernels": {k: {"ms_per_step": round(v[0] / steps, 4), "launches_per_step": v[1] / steps,
+                           "avg_us": round(1e3 * v[0] / v[1], 2)} for k, v in prof.items() if v[1]}}
+    elem = sum(g.batch * g.rows * g.cols for g in wl.groups)
+    res["hbm_passes"] = hbm_passes(prof, elem, HEADLINE_TRAFFIC if idx == 3 else None)
+    if roofline:
+        res["roofline"] = product_roofline(prof, per_kind, steps, HEADLINE_TRAFFIC)
+    del groups, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def product_roofline(prof, per_kind, steps, traffic_path):
+    """The dominant Newton-Schulz product: its algorithmic flops per launch
+    (flops per step over launches per step) over its average launch time."""
+    ms = {k: prof[k][0] + prof.get(k + "_slices", (0.0, 0))[0] for k in NS_KINDS if k in prof}
+    dom = max(ms, key=ms.get)
+    launches = prof[dom][1] + prof.get(dom + "_slices", (0.0, 0))[1]
+    avg_s = ms[dom] / launches * 1e-3
+    flop_launch = per_kind[dom] * steps / launches
+    achieved = flop_launch / avg_s / 1e12
+    traffic = measured_traffic(traffic_path)
+    return {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": round(traffic[dom]) if dom in traffic else None,
+            "flop_per_launch": flop_launch, "avg_launch_us": round(avg_s * 1e6, 1), "launches": launches}
+
+
+def hbm_passes(prof, elem, traffic_path):
+    """Algorithmic bytes per launch over the event time of the HBM passes:
+    momentum + lookahead + Frobenius partials, 12 B per element for bf16
+    gradients (G 2, M read 4 and written 4, X0 2); the scaled, decayed write,
+    6 B per element (O 2, W read 2 and written 2).  The momentum pass also
+    writes X0 transposed (2 B more per element), which the Newton-Schulz
+    products read; that is reported as bytes_moved but not counted as work."""
+    traffic = measured_traffic(traffic_path) if traffic_path else {}
+    out = {}
+    for k, per, moved in (("momentum_norm", 12, 14), ("param_update", 6, 6)):
+        if k in prof and prof[k][1]:
+            launches = prof[k][1]
+            t = prof[k][0] / launches * 1e-3
+            by = per * elem
+            out[k] = {"GBs": round(by / t / 1e9, 1), "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+                      "bytes": by, "bytes_per_element": per, "bytes_moved": moved * elem,
+                      "GBs_moved": round(moved * elem / t / 1e9, 1), "avg_us": round(t * 1e6, 1),
+                      "traffic": round(traffic[k]) if k in traffic else None}
+    return out
+
+
+def muonclip_layer_reading(mm, torch, dev, seed, steps, warmup, companions=False):
+    """The MuonClip attention layer (hidden 7168, 64 heads x 128, batch 4 x seq
+    4096): S_max on the forward's Q and K, the Muon step on W_q, W_k, W_v
+    [8192x7168] and W_o [7168x8192], then the per-head W_q / W_k rescale."""
+    from synthetic import generators as gen
     wl = gen.workload(5)
     ex = wl.extra
     B, T, H, D, dm = ex["batch"], ex["seq"], ex["heads"], ex["d_head"], ex["d_model"]
-    seed = args.seed
-
-    # ---------------- inputs (not timed)
     qk = gen.qk_inputs_torch(seed, B, T, H, D, dm, ex["n_designated"], ex["targets"], dev)
     Wqkv = gen.bulk_normal_torch((3, H * D, dm), wl.weight_std, seed + 10, dev, torch.bfloat16)
     Wqkv[0].copy_(qk["Wq"])
@@ -149,134 +372,78 @@ def main():
     s_max = torch.empty(H, dtype=torch.float32, device=dev)
     clipped = torch.empty(H, dtype=torch.int32, device=dev)
     rm_ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
 
     def step():
         mm.qkclip_rowmax(Q, K, 1.0 / math.sqrt(D), True, out=s_max, workspace=rm_ws)
         mm.muon_step(groups, hp, workspace=ws)
         mm.qkclip_rescale(Wqkv[0], Wqkv[1], s_max, D, ex["tau"], ex["alpha"], clipped=clipped)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---------------- timed region
-    mm.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    prof = mm.profile_collect()
-    mm.profile_enable(False)
-
-    n_clipped = int((clipped == 1).sum())
-    ms_per_step = 1e3 * elapsed / args.steps
-    steps_per_s = args.steps / elapsed
-
-    # ---------------- Newton-Schulz throughput and the dominant kernel's roofline
-    m, n = 7168, 8192                      # every matrix is 7168 x 8192 once oriented wide
-    n_mats = 4
-    per_iter = ns_flops(m, n)
-    ns_flop_step = n_mats * wl.ns_steps * sum(per_iter.values())
-    # a symmetric product whose last wave is split runs as two kernels: the
-    # whole tiles, then the last tiles' column halves (kind "<product>_slices")
-    product_ms = {k: prof[k][0] + prof.get(k + "_slices", (0.0, 0))[0] for k in per_iter}
-    ns_ms_step = sum(product_ms.values()) / args.steps
-    ns_tflops = ns_flop_step / (ns_ms_step * 1e-3) / 1e12
-    kernels = {k: {"total_ms": round(v[0], 4), "launches": v[1],
-                   "avg_us": round(1e3 * v[0] / v[1], 2) if v[1] else None}
-               for k, v in prof.items() if v[1]}
-    dom = max(per_iter, key=lambda k: product_ms[k])
-    dom_avg_s = product_ms[dom] / prof[dom][1] * 1e-3
-    dom_flop = n_mats * per_iter[dom]
-    achieved = dom_flop / dom_avg_s / 1e12
-    traffic = measured_traffic()
-    roofline = {"kernel": dom + (" + slices" if prof.get(dom + "_slices", (0.0, 0))[1] else ""), "bound": "mfma", "achieved": round(achieved, 1),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": round(traffic[dom]) if dom in traffic else None,
-                "measured_peak": MFMA_BF16_MEASURED_TFLOPS,
-                "frac_of_measured_peak": round(achieved / MFMA_BF16_MEASURED_TFLOPS, 4)}
-
-    # HBM passes: algorithmic bytes per launch over their event time
-    elem = 4 * m * n
-    hbm = {}
-    mom_bytes = elem * (2 + 4 + 4 + 2 + 2)      # G bf16, M r/w fp32, X0 and X0^T bf16
-    upd_bytes = elem * (2 + 2 + 2)              # O bf16, W bf16 r/w
-    for k, by in (("momentum_norm", mom_bytes), ("param_update", upd_bytes)):
-        if prof[k][1]:
-            t = prof[k][0] / prof[k][1] * 1e-3
-            hbm[k] = {"GBs": round(by / t / 1e9, 1), "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
-                      "bytes": by, "traffic": round(traffic[k]) if k in traffic else None}
-    if prof["qk_rescale"][1]:
-        # the clipped heads' rows of W_q and W_k, each read and written once
-        # (bf16); 59 MB per step here, so the pass is launch-bound
-        by = int((clipped == 1).sum()) * D * dm * 2 * 2 * 2
-        t = prof["qk_rescale"][0] / prof["qk_rescale"][1] * 1e-3
-        hbm["qk_rescale"] = {"GBs": round(by / t / 1e9, 1), "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
-                             "bytes": by, "traffic": round(traffic["qk_rescale"]) if "qk_rescale" in traffic else None}
+    elapsed, median, prof = timed_steps(mm, torch, step, steps, warmup)
+    flop, dense, per_kind, ns_ms = ns_summary(wl, prof, steps)
+    res = {"workload": "MuonClip layer: hidden 7168, 64 heads x 128, batch 4 x seq 4096; S_max, Muon step on "
+                       "W_q, W_k, W_v [8192x7168] and W_o [7168x8192], per-head rescale at tau 100",
+           "steps": steps, "warmup": warmup, "steps_per_s": round(steps / elapsed, 3),
+           "ms_per_step": round(1e3 * elapsed / steps, 3), "median_ms_per_step": round(median, 3),
+           "ns_ms_per_step": round(ns_ms, 3), "ns_tflops": round(flop / (ns_ms * 1e-3) / 1e12, 1),
+           "ns_frac_mfma_peak": round(flop / (ns_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "ns_tflops_dense_equivalent": round(dense / (ns_ms * 1e-3) / 1e12, 1),
+           "heads_clipped_per_step": int((clipped == 1).sum())}
+    res["roofline"] = product_roofline(prof, per_kind, steps, LAYER_TRAFFIC)
+    res["hbm_passes"] = hbm_passes(prof, 4 * 7168 * 8192, LAYER_TRAFFIC)
+    kern = {k: {"ms_per_step": round(v[0] / steps, 4), "launches_per_step": v[1] / steps,
+                "avg_us": round(1e3 * v[0] / v[1], 2)} for k, v in prof.items() if v[1]}
     if prof["qk_rowmax"][1]:
+        # the statistic is a max over every causal pair: 2 d B H T (T + 1) / 2 flops
         qk_flop = 2 * D * B * H * T * (T + 1) / 2
         t = prof["qk_rowmax"][0] / prof["qk_rowmax"][1] * 1e-3
-        kernels["qk_rowmax"]["tflops"] = round(qk_flop / t / 1e12, 1)
-        kernels["qk_rowmax"]["frac_mfma_peak"] = round(qk_flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-
-    out = {
-        "metric": "Muon steps/s + Newton–Schulz TFLOP/s (% bf16 MFMA peak), 1 MI355X",
-        "value": round(steps_per_s, 3),
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "MuonClip layer: hidden 7168, 64 heads x 128, batch 4 x seq 4096; "
-                               "Muon step on W_q, W_k, W_v [8192x7168] and W_o [7168x8192]",
-                   "ns_steps": wl.ns_steps, "tau": ex["tau"], "parallelism": "single GPU"},
-        "ns_tflops": round(ns_tflops, 1),
-        "ns_frac_mfma_peak": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "ns_frac_measured_mfma_peak": round(ns_tflops / MFMA_BF16_MEASURED_TFLOPS, 4),
-        "ns_ms_per_step": round(ns_ms_step, 3),
-        "roofline": roofline,
-        "hbm_passes": hbm,
-        "kernels": kernels,
-        "heads_clipped_per_step": n_clipped,
-    }
-
-    note("MuonClip layer step timed")
-    out["companion"] = companion(mm, torch, dev, seed, n_mats * m * n)
-    out["companion"]["attn_fwd"] = attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, prof["qk_rowmax"])
+        kern["qk_rowmax"]["tflops"] = round(qk_flop / t / 1e12, 1)
+        kern["qk_rowmax"]["frac_mfma_peak"] = round(qk_flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        kern["qk_rowmax"]["bytes_read"] = 2 * B * T * H * D * 2
+    if prof["qk_reduce"][1]:
+        # per-head reduction of the row-max pass's partial maxima: B H ceil(T / 256)
+        # fp32 partials read, H fp32 written; launch-bound at this size
+        by = 4 * (B * H * ((T + 255) // 256) + H)
+        t = prof["qk_reduce"][0] / prof["qk_reduce"][1] * 1e-3
+        kern["qk_reduce"]["bytes"] = by
+        kern["qk_reduce"]["GBs"] = round(by / t / 1e9, 2)
+    if prof["qk_rescale"][1]:
+        # the clipped heads' rows of W_q and W_k, each read and written once (bf16)
+        by = res["heads_clipped_per_step"] * D * dm * 2 * 2 * 2
+        t = prof["qk_rescale"][0] / prof["qk_rescale"][1] * 1e-3
+        kern["qk_rescale"]["bytes"] = by
+        kern["qk_rescale"]["GBs"] = round(by / t / 1e9, 1)
+    res["kernels"] = kern
+    if companions:
+        res["companion"] = companion(mm, torch, dev, seed, 4 * 7168 * 8192)
+        res["companion"]["attn_fwd"] = attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D,
+                                                           prof["qk_rowmax"])
     del Q, K, Wqkv, Wo, Gqkv, Go, Mqkv, Mo, ws, groups
     torch.cuda.empty_cache()
-    note("companion passes timed")
-    out["layer_hidden2048"] = config_reading(mm, torch, dev, seed, 2, args.steps, args.warmup)
-    note("hidden-2048 layer timed")
-    out["single_matrix_256x128"] = small_matrix_reading(mm, torch, dev, seed)
-    note("single 256x128 matrix timed")
-    if not args.no_other_configs:
-        k = max(2, min(3, args.steps))
-        out["other_configs"] = {"dense_decoder_24_layers": config_reading(mm, torch, dev, seed, 3, k, 1)}
-        note("24-layer decoder timed")
-        out["other_configs"]["moe_64_experts"] = config_reading(mm, torch, dev, seed, 4, k, 1)
-        note("64-expert MoE stack timed")
-        out["dion_rank128"] = dion_reading(mm, torch, dev, seed)
-        note("Dion step timed")
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, m, n, n_mats, B, T, H, D)
-    print(json.dumps(out), flush=True)
+    return res
+
+
+def copy_calibration(torch):
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    return {"copy_calibration_bytes": src.numel(), "copies": 3,
+            "copy_GBs_read_plus_write": round(2 * src.numel() / ms / 1e6, 1)}
 
 
 def blas_reference(torch, reps=10):
     """hipBLASLt (torch.matmul) on the three products of one Newton-Schulz
-    iteration at the layer's shape (4 matrices, wide 7168 x 8192), computed
-    in full (no symmetry) and without the a X / b A terms.  Operands are
-    contiguous; the result is a reference point, not part of the method."""
+    iteration at the MuonClip layer's shape (4 matrices, wide 7168 x 8192),
+    computed in full (no symmetry) and without the a X / b A terms.  Operands
+    are contiguous; the result is a reference point, not part of the method."""
     dev = torch.device("cuda:0")
     m, n, nb = 7168, 8192, 4
     g = torch.Generator(device=dev)
@@ -409,57 +576,6 @@ def dion_reading(mm, torch, dev, seed, batch=48, size=4096, rank=128, steps=3):
             "kernels": kern}
 
 
-def config_reading(mm, torch, dev, seed, idx, steps, warmup):
-    """The Muon step alone (no QK-Clip) on one of the other configurations,
-    drawn on the GPU with its recipe (bf16 params and grads, fp32 momentum;
-    grads N(0,1), low-rank-plus-noise, or low-rank-plus-noise with Zipf(1.1)
-    expert magnitudes).  A second reading of the same metric beside the
-    headline MuonClip layer, whose step is the only one that covers every
-    stage of the path."""
-    from synthetic import generators as gen
-    wl = gen.workload(idx)
-    groups = []
-    for gi, gr in enumerate(wl.groups):
-        W = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.02, seed + 100 + gi, dev, torch.bfloat16)
-        if wl.grad_kind == "normal":
-            G = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 1.0, seed + 200 + gi, dev, torch.bfloat16)
-        else:
-            mags = gen.zipf_magnitudes(gen.rng(seed + 7), gr.batch) if wl.grad_kind == "lowrank_zipf" \
-                else [1.0] * gr.batch
-            G = torch.stack([gen.lowrank_torch(gr.rows, gr.cols, seed + 200 + 1000 * gi + b, dev,
-                                               magnitude=float(mags[b])) for b in range(gr.batch)])
-        M = gen.bulk_normal_torch((gr.batch, gr.rows, gr.cols), 0.5, seed + 300 + gi, dev, torch.float32)
-        groups.append((W, G, M))
-    hp = mm.HParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=True,
-                    ns_steps=wl.ns_steps, ns_coeffs=wl.ns_coeffs, ns_eps=wl.ns_eps, rms_target=wl.rms_target)
-    ws = torch.empty(mm.workspace_size(groups), dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
-        mm.muon_step(groups, hp, workspace=ws)
-    torch.cuda.synchronize()
-    mm.profile_enable(True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        mm.muon_step(groups, hp, workspace=ws)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    prof = mm.profile_collect()
-    mm.profile_enable(False)
-    flop = 0.0
-    for gr in wl.groups:
-        m, n = min(gr.rows, gr.cols), max(gr.rows, gr.cols)
-        flop += gr.batch * wl.ns_steps * sum(ns_flops(m, n).values())
-    ns_ms = sum(prof[k][0] for k in ("ns_syrk_xxt", "ns_syrk_poly", "ns_gemm_bx",
-                                     "ns_syrk_xxt_slices", "ns_syrk_poly_slices") if k in prof) / steps
-    res = {"workload": wl.name + ": " + ", ".join(f"{g.batch} x {g.rows}x{g.cols}" for g in wl.groups),
-           "steps": steps, "steps_per_s": round(steps / el, 3), "ms_per_step": round(1e3 * el / steps, 3),
-           "ns_tflops": round(flop / (ns_ms * 1e-3) / 1e12, 1),
-           "ns_frac_mfma_peak": round(flop / (ns_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-           "kernels_ms_per_step": {k: round(v[0] / steps, 4) for k, v in prof.items() if v[1]}}
-    del groups, ws
-    torch.cuda.empty_cache()
-    return res
-
-
 def attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, rowmax_prof, reps=5):
     """The causal attention forward on the layer's Q, K and a synthetic V,
     which produces the same S_max as the separate rowmax pass.  Algorithmic
@@ -533,45 +649,127 @@ def companion(mm, torch, dev, seed, n_elem, reps=5):
     return res
 
 
-def cpu_baseline(wl, m, n, n_mats, B, T, H, D):
-    """Time the fp64 oracle on a bounded sample and extrapolate to one step:
-    one Newton-Schulz iteration, the momentum and update of one 7168 x 8192
-    matrix, and the causal logit maximum of one (batch row, head) pair."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host cores
+# ---------------------------------------------------------------------------
+
+def blas_info():
+    """Threads and vendor of the BLAS NumPy calls (threadpoolctl), or
+    numpy.show_config()'s build entry when threadpoolctl has nothing."""
+    threads, vendor = os.cpu_count() or 1, "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(i.get("num_threads", 1) for i in blas)
+            vendor = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in blas)
+    except Exception:
+        pass
+    if vendor == "unknown":
+        try:
+            import numpy as np
+            cfg = np.show_config(mode="dicts")
+            vendor = str(cfg.get("Build Dependencies", {}).get("blas", {}).get("name", "unknown"))
+        except Exception:
+            pass
+    return threads, vendor
+
+
+def cpu_baseline_decoder(seed, iters=1):
+    """Time the fp64 oracle on a bounded sample of the headline workload and
+    extrapolate to one step: per shape class of the 24-layer decoder, one
+    Newton-Schulz iteration and the momentum / lookahead / normalisation /
+    update pass of one matrix; a step is each class's matrix count times
+    (5 iterations + that pass).  Inputs are N(0, 1) draws of the class's
+    shape (the oracle's time does not depend on the values)."""
     import numpy as np
 
     from oracle import muon_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
-    g = np.random.default_rng(1)
-    X = g.standard_normal((m, n))
-    X /= np.linalg.norm(X)
-    t0 = time.perf_counter()
-    O.newton_schulz_iterate(X, 1, *wl.ns_coeffs)
-    t_iter = time.perf_counter() - t0
-    W = g.standard_normal((m, n)) * 0.02
-    M = g.standard_normal((m, n)) * 0.5
-    G = g.standard_normal((m, n))
-    t0 = time.perf_counter()
-    Mn = O.momentum_update(M, G, wl.momentum)
-    U = O.nesterov_lookahead(Mn, G, wl.momentum, True)
-    O.frobenius_normalize(U, wl.ns_eps)
-    O.param_update(W, U, wl.lr, wl.weight_decay, 18.1)
-    t_elem = time.perf_counter() - t0
-    Qs = g.standard_normal((1, T, 1, D))
-    Ks = g.standard_normal((1, T, 1, D))
-    t0 = time.perf_counter()
-    O.smax_per_head(Qs, Ks, 1 / math.sqrt(D), True)
-    t_pair = time.perf_counter() - t0
-    step_s = n_mats * (wl.ns_steps * t_iter + t_elem) + B * H * t_pair
+    from synthetic import generators as gen
+    wl = gen.workload(3)
+    threads, vendor = blas_info()
+    g = np.random.default_rng(seed)
+    step_s, parts = 0.0, []
+    t_all = time.perf_counter()
+    for gr in wl.groups:
+        W = g.standard_normal((gr.rows, gr.cols)) * 0.02
+        M = g.standard_normal((gr.rows, gr.cols)) * 0.5
+        G = g.standard_normal((gr.rows, gr.cols))
+        t0 = time.perf_counter()
+        Mn = O.momentum_update(M, G, wl.momentum)
+        U = O.nesterov_lookahead(Mn, G, wl.momentum, True)
+        X, _ = O.to_wide(U)
+        X = O.frobenius_normalize(X, wl.ns_eps)
+        t_elem = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        X = O.newton_schulz_iterate(X, iters, *wl.ns_coeffs)
+        t_iter = (time.perf_counter() - t0) / iters
+        t0 = time.perf_counter()
+        O.param_update(W, X.T if gr.rows > gr.cols else X, wl.lr, wl.weight_decay,
+                       O.update_scale(gr.rows, gr.cols))
+        t_elem += time.perf_counter() - t0
+        step_s += gr.batch * (wl.ns_steps * t_iter + t_elem)
+        parts.append(f"{gr.rows}x{gr.cols}: {t_iter:.2f} s per iteration + {t_elem:.2f} s")
+    sample_s = time.perf_counter() - t_all
     return {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle: 1 Newton-Schulz iteration ({t_iter:.2f} s) and the "
-                       f"momentum/normalise/update pass ({t_elem:.2f} s) of one 7168x8192 matrix, "
-                       f"S_max of one (batch row, head) pair ({t_pair:.2f} s); extrapolated to "
-                       f"{n_mats} matrices x {wl.ns_steps} iterations + {B * H} pairs"),
-            "seconds_per_step": round(step_s, 2)}
+            "blas": vendor,
+            "sample": (f"fp64 NumPy oracle, one matrix per shape class of the 24-layer decoder ("
+                       + "; ".join(parts) + f"), {sample_s:.1f} s in all; extrapolated to "
+                       f"{sum(g.batch for g in wl.groups)} matrices x {wl.ns_steps} iterations"),
+            "seconds_per_step": round(step_s, 1)}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+
+KERNEL_NAMES = (
+    ("ns_gemm_kernel<256, 256, 0>", "ns_syrk_xxt"), ("ns_gemm_kernel<256, 256, 1>", "ns_syrk_poly"),
+    ("ns_gemm_kernel<256, 256, 2>", "ns_gemm_bx"), ("ns_gemm_kernel<128, 128, 0>", "ns_syrk_xxt [128]"),
+    ("ns_gemm_kernel<128, 128, 1>", "ns_syrk_poly [128]"), ("ns_gemm_kernel<128, 128, 2>", "ns_gemm_bx [128]"),
+    ("ns_gemm_kernel<256, 128, 0>", "ns_syrk_xxt_slices"), ("ns_gemm_kernel<256, 128, 1>", "ns_syrk_poly_slices"),
+    ("momentum_norm_kernel", "momentum_norm"), ("norm_finalize_kernel", "norm_finalize"),
+    ("param_update_kernel", "param_update"), ("qk_rowmax_kernel", "qk_rowmax"), ("qk_reduce_kernel", "qk_reduce"),
+    ("qk_rescale_kernel", "qk_rescale"), ("small_step_kernel", "small_step"), ("thin_gram_kernel", "ns_thin_gram"),
+    ("thin_poly_kernel", "ns_thin_poly"), ("thin_bx_kernel", "ns_thin_bx"), ("adamw_kernel", "adamw"),
+    ("attn_fwd_kernel", "attn_fwd"), ("mfma_probe_kernel", "mfma_probe"), ("dion_", "dion"))
+
+
+def short_name(kernel):
+    flat = kernel.replace(" ", "")
+    for pat, name in KERNEL_NAMES:
+        if pat.replace(" ", "") in flat:
+            return name
+    return "(other: " + kernel[:40] + ")"
+
+
+def summarize_profile(paths):
+    """Per-kernel summary of rocprofv3 CSV output: a kernel trace
+    (*_kernel_trace.csv: calls and average / min / max duration) or a counter
+    collection (*_counter_collection.csv: mean counter value per dispatch)."""
+    import csv
+    from collections import defaultdict
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        if not rows:
+            continue
+        print(f"# {os.path.basename(path)}")
+        if "Start_Timestamp" in rows[0]:
+            d = defaultdict(list)
+            for r in rows:
+                d[short_name(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            tot = sum(sum(v) for v in d.values())
+            print(f"# {'kernel':28s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>7s}")
+            for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+                print(f"  {k:28s} {len(v):7d} {sum(v) / len(v):10.1f} {min(v):10.1f} {max(v):10.1f} "
+                      f"{100 * sum(v) / tot:7.2f}")
+        else:
+            d = defaultdict(list)
+            for r in rows:
+                d[(short_name(r["Kernel_Name"]), r["Counter_Name"])].append(float(r["Counter_Value"]))
+            print(f"# {'kernel':28s} {'counter':>12s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
+            for (k, c), v in sorted(d.items()):
+                print(f"  {k:28s} {c:>12s} {len(v):10d} {sum(v) / len(v):18.1f}")
 
 
 if __name__ == "__main__":

@@ -111,7 +111,11 @@ typedef struct {
  * one parameter dtype: momentum update and Nesterov lookahead fused with the
  * Frobenius partial sums in one pass; Newton-Schulz on bf16 MFMA with fp32
  * accumulation, every same-shape matrix of every group batched into one
- * launch per stage; then the scaled, decayed parameter write.
+ * launch per stage; then the scaled, decayed parameter write.  X, A = X X^T
+ * and B = b A + c A A are stored in bf16 between products, except for wide
+ * views of at most 96 rows, whose A and B are kept to about 2^-17 (a bf16
+ * pair hi + lo): with so few singular values a bf16 rounding of B is not
+ * averaged over directions.
  *   groups:          host array of n_groups descriptors (1..MUON_MAX_GROUPS)
  *   param_dtype:     MUON_DTYPE_F32 or MUON_DTYPE_BF16 (grads share it)
  *   hp:              host pointer, see muon_hparams_t
@@ -298,6 +302,15 @@ int dion_step(void* param, int dtype, const void* grad, float* momentum, float* 
 
 /* -------------------------------------------------------------- diagnostics */
 const char* muon_status_string(int status);
+
+/* Matrix-core rate probe (not part of the optimizer): `blocks` workgroups of
+ * 256 threads, each wave issuing 4 * iters v_mfma_f32_32x32x16_bf16 on
+ * register operands, no memory traffic in the loop; 32768 flop per MFMA, so
+ * blocks * 4 * 4 * iters * 32768 flop per launch.  Time it with events on
+ * `stream` to get the sustained bf16 MFMA rate at the clock the chip holds
+ * under that load.  sink: device float[blocks], written once per block.
+ * MUON_ERR_INVALID_ARG for blocks outside 1..2^20, iters < 1 or a null sink. */
+int muon_mfma_probe(int blocks, int iters, float* sink, hipStream_t stream);
 
 /* Optional per-kernel timing with HIP events recorded around every launch
  * the library makes on the caller's stream.  muon_profile_enable(1) clears

@@ -115,6 +115,8 @@ def load_library() -> ctypes.CDLL:
     lib.dion_step.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i64, f32, f32, vp, sz, vp]
     lib.dion_step.restype = i32
     lib.adamw_step.restype = i32
+    lib.muon_mfma_probe.argtypes = [i32, i32, vp, vp]
+    lib.muon_mfma_probe.restype = i32
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_profile_enable.argtypes = [i32]
@@ -176,9 +178,13 @@ def _as3d(t):
             raise ValueError("matrices must be row-major contiguous")
         return 1, t.shape[0], t.shape[1], t.shape[0] * t.shape[1]
     if t.dim() == 3:
-        if t.stride(2) != 1 or t.stride(1) != t.shape[2] or t.stride(0) < t.shape[1] * t.shape[2]:
+        b, r, c = t.shape
+        # a stride along a dimension of extent 1 is never used (NumPy gives
+        # inserted axes stride 0)
+        row_ok = (t.stride(2) == 1 or c == 1) and (t.stride(1) == c or r == 1)
+        if not row_ok or (b > 1 and t.stride(0) < r * c):
             raise ValueError("each matrix must be row-major contiguous")
-        return t.shape[0], t.shape[1], t.shape[2], t.stride(0)
+        return b, r, c, (t.stride(0) if b > 1 else r * c)
     raise ValueError("expected a 2-D or 3-D tensor")
 
 
@@ -501,6 +507,17 @@ def dion_step(param, grad, momentum, q, *, lr: float, mu: float = 0.95, workspac
                          q.data_ptr(), b, r, c, rank, st, lr, mu, workspace.data_ptr(), workspace.numel(),
                          _stream()), "dion_step")
     return workspace
+
+
+def mfma_probe(blocks: int, iters: int, sink):
+    """Launch the register-only bf16 MFMA loop on the current stream (see
+    muon_mfma_probe); sink: a float32 device tensor of >= blocks elements.
+    Returns the launch's flop count."""
+    _need_cuda(sink)
+    if sink.dtype != _torch().float32 or sink.numel() < blocks:
+        raise ValueError("sink must be a float32 tensor of at least `blocks` elements")
+    _check(load_library().muon_mfma_probe(blocks, iters, sink.data_ptr(), _stream()), "muon_mfma_probe")
+    return blocks * 4 * 4 * iters * 32768
 
 
 def profile_enable(on: bool = True):

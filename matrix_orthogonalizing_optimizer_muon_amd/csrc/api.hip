@@ -42,14 +42,14 @@ void prof_begin(int kind, hipStream_t s) {
   if (!g_prof_on) return;
   g_open_kind = kind;
   g_open_start = pool_get();
-  if (g_open_start) hipEventRecord(g_open_start, s);
+  if (g_open_start) (void)hipEventRecord(g_open_start, s);
 }
 
 void prof_end(int kind, hipStream_t s) {
   if (!g_prof_on || !g_open_start || g_open_kind != kind) return;
   hipEvent_t e = pool_get();
   if (!e) return;
-  hipEventRecord(e, s);
+  (void)hipEventRecord(e, s);
   g_prof.push_back({kind, g_open_start, e});
   g_open_start = nullptr;
   g_open_kind = -1;
@@ -73,8 +73,15 @@ struct Plan {
   int mp, np;     // padded wide view (multiples of tile)
   int rp, cp;     // padded original layout
   int tiles_r, tiles_c, mom_tiles;
-  size_t off_X[2], off_Xt[2], off_A, off_B, off_part, off_inv;
+  bool thin;      // m <= kThinMaxM and too long for the single-workgroup step
+  int mq, chunk, nchunk;   // thin: rows in 32-blocks, Gram partial chunking
+  size_t off_X[2], off_Xt[2], off_A, off_B, off_part, off_inv, off_thin_part, off_thin_B;
 };
+
+// Groups whose wide view fits the single-workgroup step (X and A in LDS).
+bool small_ok(int rows, int cols) {
+  return std::min(rows, cols) <= kSmallMaxM && std::max(rows, cols) <= kSmallMaxN;
+}
 
 Plan make_plan(int batch, int rows, int cols, int64_t bstride, size_t& cursor) {
   Plan p{};
@@ -93,8 +100,9 @@ Plan make_plan(int batch, int rows, int cols, int64_t bstride, size_t& cursor) {
   p.tiles_r = p.rp / 64;
   p.tiles_c = p.cp / 64;
   p.mom_tiles = p.tiles_r * p.tiles_c;
+  p.thin = p.m <= kThinMaxM && !small_ok(rows, cols);
   const size_t xb = static_cast<size_t>(batch) * p.mp * p.np * sizeof(bf16_t);
-  const size_t ab = static_cast<size_t>(batch) * p.mp * p.mp * sizeof(bf16_t);
+  const size_t ab = p.thin ? 0 : static_cast<size_t>(batch) * p.mp * p.mp * sizeof(bf16_t);
   for (int k = 0; k < 2; ++k) {
     p.off_X[k] = cursor;
     cursor = align_up(cursor + xb);
@@ -109,6 +117,18 @@ Plan make_plan(int batch, int rows, int cols, int64_t bstride, size_t& cursor) {
   cursor = align_up(cursor + static_cast<size_t>(batch) * p.mom_tiles * sizeof(double));
   p.off_inv = cursor;
   cursor = align_up(cursor + static_cast<size_t>(batch) * sizeof(float));
+  if (p.thin) {
+    // Gram partials over column chunks of 512 columns or more, at most 64
+    // chunks per matrix; then B, both fp32
+    p.mq = round_up(p.m, 32);
+    p.chunk = 512 * ((p.np + 512 * 64 - 1) / (512 * 64));
+    p.nchunk = (p.np + p.chunk - 1) / p.chunk;
+    const size_t sq = static_cast<size_t>(p.mq) * p.mq * sizeof(float);
+    p.off_thin_part = cursor;
+    cursor = align_up(cursor + static_cast<size_t>(batch) * p.nchunk * sq);
+    p.off_thin_B = cursor;
+    cursor = align_up(cursor + static_cast<size_t>(batch) * sq);
+  }
   return p;
 }
 
@@ -227,11 +247,6 @@ struct FinalOut {
 
 enum Stage { STAGE_SYRK = 0, STAGE_POLY = 1, STAGE_BX = 2 };
 
-// Groups whose wide view fits the single-workgroup step (X and A in LDS).
-bool small_ok(int rows, int cols) {
-  return std::min(rows, cols) <= kSmallMaxM && std::max(rows, cols) <= kSmallMaxN;
-}
-
 // Compute units of the current device (one GEMM block runs per CU at a time);
 // 0 if the query fails, which turns the last-wave split off.
 int cu_count() {
@@ -305,11 +320,92 @@ GemmProb make_prob(const Plan& p, int stage, int t, int steps, float a, float b,
   return q;
 }
 
+// One Newton-Schulz step t of every thin group: Gram partials, B, X'.
+int run_thin(const std::vector<Plan>& plans, int t, int steps, float a, float b, float c, void* ws,
+             const std::vector<FinalOut>* fins, hipStream_t s) {
+  ThinLaunch L{};
+  L.first = (t == 0) ? 1 : 0;
+  L.a = a;
+  L.b = b;
+  L.c = c;
+  std::vector<int> ids;
+  for (size_t g = 0; g < plans.size(); ++g)
+    if (plans[g].thin) ids.push_back(static_cast<int>(g));
+  if (ids.empty()) return MUON_OK;
+  const int cur = t & 1, nxt = cur ^ 1;
+  const bool last = (t == steps - 1);
+  L.ngroups = static_cast<int>(ids.size());
+  for (size_t k = 0; k < ids.size(); ++k) {
+    const Plan& p = plans[ids[k]];
+    ThinGroup& q = L.g[k];
+    q.X = at<bf16_t>(ws, p.off_X[cur]);
+    q.x_stride = static_cast<int64_t>(p.mp) * p.np;
+    q.np = p.np;
+    q.mb = p.mq / 32;
+    q.chunk = p.chunk;
+    q.nchunk = p.nchunk;
+    q.part = at<float>(ws, p.off_thin_part);
+    q.Bm = at<float>(ws, p.off_thin_B);
+    q.inv = at<float>(ws, p.off_inv);
+    q.batch = p.batch;
+    const FinalOut* fin = fins ? &(*fins)[ids[k]] : nullptr;
+    if (!last) {
+      q.D = at<bf16_t>(ws, p.off_X[nxt]);
+      q.d_stride = q.x_stride;
+      q.d_ld = p.np;
+      q.d_trans = 0;
+      q.d_rvalid = p.mq;
+      q.d_cvalid = p.np;
+      q.d_vec = 1;
+    } else if (fin && fin->ptr) {
+      // straight into the caller's dense output, in the matrix's own layout
+      q.D = fin->ptr;
+      q.d_stride = fin->stride;
+      q.d_ld = fin->ld;
+      q.d_trans = p.tall ? 1 : 0;
+      q.d_rvalid = p.tall ? p.n : p.m;
+      q.d_cvalid = p.tall ? p.m : p.n;
+      q.d_vec = (fin->ld % 8 == 0) && aligned(fin->ptr, 16) && (fin->stride % 8 == 0);
+    } else if (!p.tall) {
+      q.D = at<bf16_t>(ws, p.off_X[nxt]);
+      q.d_stride = q.x_stride;
+      q.d_ld = p.np;
+      q.d_trans = 0;
+      q.d_rvalid = p.mq;
+      q.d_cvalid = p.np;
+      q.d_vec = 1;
+    } else {
+      // the workspace's transposed buffer [np][mp], the tall matrix's layout
+      q.D = at<bf16_t>(ws, p.off_Xt[nxt]);
+      q.d_stride = q.x_stride;
+      q.d_ld = p.mp;
+      q.d_trans = 1;
+      q.d_rvalid = p.np;
+      q.d_cvalid = p.mq;
+      q.d_vec = 1;
+    }
+  }
+  static const int kinds[3] = {KIND_THIN_GRAM, KIND_THIN_POLY, KIND_THIN_BX};
+  for (int stage = 0; stage < 3; ++stage) {
+    int blocks = 0;
+    for (size_t k = 0; k < ids.size(); ++k) {
+      const Plan& p = plans[ids[k]];
+      L.prefix[k] = blocks;
+      blocks += p.batch * (stage == 0 ? p.nchunk : stage == 1 ? 1 : p.np / 128);
+    }
+    L.prefix[ids.size()] = blocks;
+    MUON_LAUNCH(kinds[stage], s, launch_thin(L, stage, blocks, s));
+  }
+  return MUON_OK;
+}
+
 int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c, void* ws,
            const std::vector<FinalOut>* fins, hipStream_t s) {
   static const int kinds[3] = {KIND_NS_SYRK, KIND_NS_POLY, KIND_NS_BX};
   static const int slice_kinds[3] = {KIND_NS_SYRK_SLICES, KIND_NS_POLY_SLICES, KIND_NS_BX};
   for (int t = 0; t < steps; ++t) {
+    int st = run_thin(plans, t, steps, a, b, c, ws, fins, s);
+    if (st != MUON_OK) return st;
     for (int stage = 0; stage < 3; ++stage) {
       if (stage == STAGE_POLY && c == 0.0f) continue;
       for (int tile : {256, 128}) {
@@ -319,7 +415,7 @@ int run_ns(const std::vector<Plan>& plans, int steps, float a, float b, float c,
         // dispatched last, which set the launch's tail, are the shortest
         std::vector<int> order;
         for (size_t g = 0; g < plans.size(); ++g)
-          if (plans[g].tile == tile) order.push_back(static_cast<int>(g));
+          if (plans[g].tile == tile && !plans[g].thin) order.push_back(static_cast<int>(g));
         auto klen = [&](int g) { return stage == STAGE_SYRK ? plans[g].np : plans[g].mp; };
         std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return klen(x) > klen(y); });
         for (int g : order) {
@@ -844,6 +940,12 @@ int dion_step(void* param, int dtype, const void* grad, float* momentum, float* 
   return MUON_OK;
 }
 
+int muon_mfma_probe(int blocks, int iters, float* sink, hipStream_t stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || !sink) return MUON_ERR_INVALID_ARG;
+  if (launch_mfma_probe(blocks, iters, sink, stream) != hipSuccess) return MUON_ERR_HIP;
+  return MUON_OK;
+}
+
 int muon_profile_enable(int on) {
   for (auto& r : g_prof) {
     g_event_pool.push_back(r.a);
@@ -877,7 +979,8 @@ const char* muon_kernel_kind_name(int kind) {
                                           "qk_rescale",    "adamw",         "attn_fwd",
                                           "ns_syrk_xxt_slices", "ns_syrk_poly_slices", "small_step",
                                           "dion_bq",       "dion_gram",     "dion_chol",   "dion_pl",
-                                          "dion_btp",      "dion_colnorm",  "dion_update"};
+                                          "dion_btp",      "dion_colnorm",  "dion_update",
+                                          "ns_thin_gram",  "ns_thin_poly",  "ns_thin_bx"};
   if (kind < 0 || kind >= KIND_COUNT) return "unknown";
   return names[kind];
 }

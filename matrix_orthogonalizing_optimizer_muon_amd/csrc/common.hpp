@@ -88,7 +88,10 @@ enum KernelKind {
   KIND_DION_BTP = 18,
   KIND_DION_COLNORM = 19,
   KIND_DION_UPDATE = 20,
-  KIND_COUNT = 21
+  KIND_THIN_GRAM = 21,
+  KIND_THIN_POLY = 22,
+  KIND_THIN_BX = 23,
+  KIND_COUNT = 24
 };
 
 // ---------------------------------------------------------------------------
@@ -221,6 +224,37 @@ struct SmallLaunch {
   float a, b, c;
 };
 
+// Newton-Schulz for thin matrices (wide view m <= kThinMaxM rows, too long
+// for the single-workgroup step): A and B kept in fp32, X in bf16.
+constexpr int kThinMaxM = 96;
+constexpr int kThinMaxMB = kThinMaxM / 32;
+
+struct ThinGroup {
+  const bf16_t* X;    // current iterate, wide [mp][np] bf16, ld np, zero-padded
+  int64_t x_stride;   // elements between matrices of X
+  int np;             // padded n, a multiple of 128
+  int mb;             // 32-row blocks: mq = 32 mb >= m
+  int chunk, nchunk;  // Gram partials: columns per chunk (multiple of 128), chunks
+  float* part;        // fp32 [batch][nchunk][mq][mq]
+  float* Bm;          // fp32 [batch][mq][mq]
+  const float* inv;   // 1 / (||U||_F + eps) per matrix (applied on the first step)
+  bf16_t* D;          // destination of X' (row-major [i][j], or [j][i] if d_trans)
+  int64_t d_stride;
+  int d_ld;
+  int d_trans;
+  int d_rvalid, d_cvalid;  // rows / columns of D written (D's own layout)
+  int d_vec;          // d_ld % 8 == 0, d_stride % 8 == 0, D 16-byte aligned
+  int batch;
+};
+
+struct ThinLaunch {
+  int ngroups;
+  int prefix[kMaxProbs + 1];  // block prefix over groups (per launch)
+  ThinGroup g[kMaxProbs];
+  int first;                  // first Newton-Schulz step: scale by inv
+  float a, b, c;
+};
+
 // Dion's rank-r step: one argument block for every launch of a step; the
 // GEMM launches set src / bsrc / dst to their operands.
 enum DionMode { DION_BQ = 0, DION_PL = 1, DION_BTP = 2, DION_UPD = 3 };
@@ -257,6 +291,9 @@ hipError_t launch_ns_gemm(const GemmLaunch& L, int tile, int stage, int nblocks,
 hipError_t launch_ns_gemm_slices(const GemmLaunch& L, int stage, int nblocks, hipStream_t s);
 hipError_t launch_param_update(const UpdateLaunch& L, int param_dtype, int64_t nblocks, hipStream_t s);
 hipError_t launch_small_step(const SmallLaunch& L, int dtype, int nmats, hipStream_t s);
+// stage 0: Gram partials (one wave per matrix and chunk), 1: B per matrix,
+// 2: X' per 128 columns
+hipError_t launch_thin(const ThinLaunch& L, int stage, int nblocks, hipStream_t s);
 hipError_t launch_dion_gemm(const DionArgs& A, int mode, int dtype, int batch, hipStream_t s);
 hipError_t launch_dion_gram(const DionArgs& A, int batch, hipStream_t s);
 hipError_t launch_dion_gram_reduce(const DionArgs& A, int batch, hipStream_t s);
@@ -319,6 +356,10 @@ struct AdamWLaunch {
   AdamWTensor t[kAdamWMaxTensors];
 };
 hipError_t launch_adamw(const AdamWLaunch& A, int dtype, int blocks, hipStream_t s);
+
+// Register-only bf16 MFMA loop (probe.hip): 256-thread blocks, each wave
+// issuing 4 x iters v_mfma_f32_32x32x16_bf16.
+hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s);
 
 // Profiler hooks (api.hip).
 void prof_begin(int kind, hipStream_t s);

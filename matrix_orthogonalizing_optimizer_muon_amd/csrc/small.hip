@@ -10,7 +10,13 @@
 //           the first iteration works on s X0, folded into its products)
 //   W <- (1 - lr wd) W - lr scale O                     ("MuonClip", section 03)
 // with the rounding points of the tiled path: bf16 operands, fp32
-// accumulation, A, B and X rounded to bf16 once per product.
+// accumulation, A, B and X rounded to bf16 once per product.  Matrices with
+// at most kThinMaxM rows in the wide view keep A and B to about 2^-17
+// instead, as a bf16 pair hi + lo (hi = bf16(v), lo = bf16(v - hi)), the way
+// the thin tiled path does: with so few rows, a bf16 rounding of B moves
+// every singular value the same way and is not averaged out.  Their products
+// add the cross terms, A A ~ Ahi Ahi^T + Ahi Alo^T + Alo Ahi^T and
+// B X ~ Bhi X + Blo X.
 //
 // X (at most 128 x 256) and A / B (at most 128 x 128) stay in LDS for the
 // whole iteration, so a small matrix costs one launch instead of the
@@ -125,8 +131,9 @@ __device__ __forceinline__ void store8(T* p, const f32x8_t& v) {
 //     roles), whose accumulators are 4 consecutive columns of a row of X'.
 template <typename T, int MB>
 __device__ __forceinline__ void small_body(const SmallLaunch& L, const SmallGroup& g, int mat, bf16_t* sX,
-                                           bf16_t* sA, double* red) {
+                                           bf16_t* sA, bf16_t* sAl, double* red) {
   constexpr int mp = 32 * MB;
+  constexpr bool SPLIT = MB <= kThinMaxMB;   // A and B as bf16 pairs (sA hi, sAl lo)
   constexpr int pa = mp + 8;                 // A / B row pitch: 16-byte rows, conflict-free fragment reads
   constexpr int nkm = mp / 16;               // k steps of the m x m contractions
   constexpr int NBLK = MB * MB;              // 32 x 32 blocks of an m x m product
@@ -360,8 +367,29 @@ __device__ __forceinline__ void small_body(const SmallLaunch& L, const SmallGrou
         static_for<4>([&](auto q) {
           constexpr int Q = decltype(q)::value;
           const f32x4_t v{acc[R][4 * Q], acc[R][4 * Q + 1], acc[R][4 * Q + 2], acc[R][4 * Q + 3]};
-          *reinterpret_cast<u32x2_t*>(sA + tpos(R, Q)) = pack4(v);
+          const u32x2_t hi = pack4(v);
+          *reinterpret_cast<u32x2_t*>(sA + tpos(R, Q)) = hi;
+          if constexpr (SPLIT) *reinterpret_cast<u32x2_t*>(sAl + tpos(R, Q)) = pack4(v - unpack4(hi));
         });
+      }
+    });
+  };
+  // A A^T from the pair planes: Ahi Ahi^T + Ahi Alo^T + Alo Ahi^T
+  auto sym_product_split = [&](f32x16_t (&acc)[2]) {
+    static_for<2>([&](auto r) {
+      constexpr int R = decltype(r)::value;
+      acc[R] = f32x16_t{};
+      if (R < mine) {
+        const int oa = (bi[R] * 32 + frow) * pa + fk, ob = (bj[R] * 32 + frow) * pa + fk;
+        for (int kk = 0; kk < nkm; ++kk) {
+          const bf16x8_t fah = *reinterpret_cast<const bf16x8_t*>(sA + oa + 16 * kk);
+          const bf16x8_t fal = *reinterpret_cast<const bf16x8_t*>(sAl + oa + 16 * kk);
+          const bf16x8_t fbh = *reinterpret_cast<const bf16x8_t*>(sA + ob + 16 * kk);
+          const bf16x8_t fbl = *reinterpret_cast<const bf16x8_t*>(sAl + ob + 16 * kk);
+          acc[R] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fah, fbh, acc[R], 0, 0, 0);
+          acc[R] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fah, fbl, acc[R], 0, 0, 0);
+          acc[R] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fal, fbh, acc[R], 0, 0, 0);
+        }
       }
     });
   };
@@ -379,13 +407,15 @@ __device__ __forceinline__ void small_body(const SmallLaunch& L, const SmallGrou
     // B = c A A^T + b A, over A in place once every wave has read it.  The
     // element stored at (j, i) is c (A A^T)_ij + b A_ji, read from that place.
     if (!cubic) {
-      sym_product(sA, pa, nkm, acc);
+      if constexpr (SPLIT) sym_product_split(acc);
+      else sym_product(sA, pa, nkm, acc);
       static_for<2>([&](auto r) {
         constexpr int R = decltype(r)::value;
         if (R < mine) {
           static_for<4>([&](auto q) {
             constexpr int Q = decltype(q)::value;
-            const f32x4_t a = unpack4(*reinterpret_cast<const u32x2_t*>(sA + tpos(R, Q)));
+            f32x4_t a = unpack4(*reinterpret_cast<const u32x2_t*>(sA + tpos(R, Q)));
+            if constexpr (SPLIT) a += unpack4(*reinterpret_cast<const u32x2_t*>(sAl + tpos(R, Q)));
             static_for<4>([&](auto x) {
               constexpr int E = decltype(x)::value;
               acc[R][4 * Q + E] = fmaf(L.b, a[E], L.c * acc[R][4 * Q + E]);
@@ -409,7 +439,8 @@ __device__ __forceinline__ void small_body(const SmallLaunch& L, const SmallGrou
     if (jb < nb) {
       const bf16_t* xcol = sX + fk * px + jb * 32 + frow;   // X[k][jb 32 + frow], k = fk + ..
       const bf16_t* prow = sA + frow * pa + fk;             // P[r 32 + frow][k], k = fk + ..
-      bf16x8_t fx[2], fp[2][MB];
+      const bf16_t* prowl = sAl + frow * pa + fk;           // its lo plane (SPLIT)
+      bf16x8_t fx[2], fp[2][MB], fl[2][MB];
       auto ld = [&](auto slot, auto kstep) {
         constexpr int SL = decltype(slot)::value, K0 = 16 * decltype(kstep)::value;
         u16x8_t w;
@@ -421,6 +452,7 @@ __device__ __forceinline__ void small_body(const SmallLaunch& L, const SmallGrou
         static_for<MB>([&](auto r) {
           constexpr int R = decltype(r)::value;
           fp[SL][R] = *reinterpret_cast<const bf16x8_t*>(prow + R * 32 * pa + K0);
+          if constexpr (SPLIT) fl[SL][R] = *reinterpret_cast<const bf16x8_t*>(prowl + R * 32 * pa + K0);
         });
       };
       ld(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -430,6 +462,7 @@ __device__ __forceinline__ void small_body(const SmallLaunch& L, const SmallGrou
         static_for<MB>([&](auto r) {
           constexpr int R = decltype(r)::value;
           xa[R] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[KS & 1], fp[KS & 1][R], xa[R], 0, 0, 0);
+          if constexpr (SPLIT) xa[R] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[KS & 1], fl[KS & 1][R], xa[R], 0, 0, 0);
         });
       });
       static_for<MB>([&](auto r) {
@@ -541,6 +574,7 @@ template <typename T>
 __global__ __launch_bounds__(kNT) void small_step_kernel(SmallLaunch L) {
   __shared__ __attribute__((aligned(16))) bf16_t sX[kSmallMaxM * kPX];
   __shared__ __attribute__((aligned(16))) bf16_t sA[kSmallMaxM * kPA];
+  __shared__ __attribute__((aligned(16))) bf16_t sAl[kThinMaxM * (kThinMaxM + 8)];
   __shared__ double red[kNT / 64];
 
   int gi = 0;
@@ -548,10 +582,10 @@ __global__ __launch_bounds__(kNT) void small_step_kernel(SmallLaunch L) {
   const SmallGroup& g = L.g[gi];
   const int mat = blockIdx.x - L.prefix[gi];
   switch ((g.m + 31) / 32) {
-    case 1: small_body<T, 1>(L, g, mat, sX, sA, red); break;
-    case 2: small_body<T, 2>(L, g, mat, sX, sA, red); break;
-    case 3: small_body<T, 3>(L, g, mat, sX, sA, red); break;
-    default: small_body<T, 4>(L, g, mat, sX, sA, red); break;
+    case 1: small_body<T, 1>(L, g, mat, sX, sA, sAl, red); break;
+    case 2: small_body<T, 2>(L, g, mat, sX, sA, sAl, red); break;
+    case 3: small_body<T, 3>(L, g, mat, sX, sA, sAl, red); break;
+    default: small_body<T, 4>(L, g, mat, sX, sA, sAl, red); break;
   }
 }
 

@@ -69,6 +69,35 @@ def low_rank_plus_noise(g: np.random.Generator, rows: int, cols: int,
     return G
 
 
+def with_spectrum(g: np.random.Generator, rows: int, cols: int, sigma) -> np.ndarray:
+    """A rows x cols matrix whose singular values are exactly `sigma` (length
+    min(rows, cols)) up to float64 rounding: diag(sigma) between two fast
+    orthogonal transforms (the orthonormal DCT-II along each side) with
+    seeded random sign flips of the rows and columns.  O(rows cols log) work,
+    so full-size spectra stay cheap to draw."""
+    from scipy.fft import dct
+    k = min(rows, cols)
+    sigma = np.asarray(sigma, dtype=np.float64)
+    assert sigma.shape == (k,)
+    Z = np.zeros((rows, cols))
+    Z[np.arange(k), np.arange(k)] = sigma
+    Z = dct(Z, type=2, norm="ortho", axis=0)
+    Z = dct(Z, type=2, norm="ortho", axis=1)
+    sr = np.where(g.random(rows) < 0.5, -1.0, 1.0)
+    sc = np.where(g.random(cols) < 0.5, -1.0, 1.0)
+    return np.ascontiguousarray((Z * sr[:, None]) * sc[None, :])
+
+
+def log_spaced_levels(k: int, levels: int = 16, cond: float = 1000.0) -> np.ndarray:
+    """k singular values on `levels` log-spaced levels from 1 down to 1/cond
+    (the interactive Newton-Schulz demo's spread), each level repeated
+    k / levels times (the remainder on the top levels)."""
+    lv = np.logspace(0.0, -np.log10(cond), levels)
+    reps = np.full(levels, k // levels)
+    reps[: k % levels] += 1
+    return np.repeat(lv, reps)
+
+
 def zipf_magnitudes(g: np.random.Generator, n: int, s: float = 1.1) -> np.ndarray:
     """Per-expert magnitude rank^-s over a seeded permutation of ranks 1..n
     (the largest is 1)."""

@@ -2,10 +2,9 @@
 identical seeded inputs.
 
 Tolerances (stated per stage, on identical inputs):
-  * Newton-Schulz output: relative Frobenius error <= 2e-2 per matrix
-    (bf16 MFMA operands, fp32 accumulation; CPU emulation of the same
-    rounding points sits at 0.9-1.5e-2); degenerate and thin shapes follow
-    ns_tolerance (5e-2 below 8 rows, 3e-2 for 8-47 rows with n >= 8 m).
+  * Newton-Schulz output: relative Frobenius error <= 2e-2 per matrix, every
+    shape (bf16 MFMA operands, fp32 accumulation; A and B kept in fp32 for
+    wide views of at most 96 rows).
   * momentum (fp32): relative Frobenius error <= 1e-5; X0 = bf16(U): every
     element a faithful bf16 rounding of U within the fp32 error bound of its
     two fused multiply-adds; 1/||U||: rel <= 1e-5.
@@ -57,27 +56,19 @@ def widen(a, dtype):
 # ---------------------------------------------------------------------------
 
 def ns_tolerance(rows, cols):
-    """2e-2 relative Frobenius error for bf16-MFMA Newton-Schulz.  A matrix
-    with one or two singular values has no averaging over directions: the
-    bf16 rounding of its 1x1 / 2x2 Gram and polynomial matrices moves the
-    single trajectory sigma -> p(sigma) directly, and |p'| ~ 1.1-1.3 along it
-    over five steps; a CPU emulation of the same rounding points reaches
-    2.0-2.8e-2 on such inputs.  Those degenerate shapes are held to 5e-2.
-    Thin matrices with 8 <= min(rows, cols) < 48 and a long other side (e.g.
-    33 x 777, singular values within a factor 1.5 of each other) emulate at
-    1.4-2.4e-2 and are held to 3e-2; from 48 rows on the emulation stays
-    below 1.9e-2."""
-    m, n = min(rows, cols), max(rows, cols)
-    if m < 8:
-        return 5e-2
-    if m < 48 and n >= 8 * m:
-        return 3e-2
+    """2e-2 relative Frobenius error for bf16-MFMA Newton-Schulz, the stated
+    tolerance, for every shape.  (Matrices with at most 96 rows in the wide
+    view keep A and B in fp32, as a bf16 hi + lo pair: with one or a few
+    singular values a bf16 rounding of B is not averaged over directions.)"""
     return 2e-2
 
 
-NS_SHAPES = [(96, 160), (200, 72), (128, 128), (1, 37), (37, 1), (300, 600), (640, 520), (520, 1100),
+NS_SHAPES = [(96, 160), (200, 72), (128, 128), (1, 37), (37, 1), (250, 1), (300, 600), (640, 520), (520, 1100),
              # long contractions over few output tiles (K up to 16 x the tile rows)
-             (300, 2100), (4096, 256), (512, 2048)]
+             (300, 2100), (4096, 256), (512, 2048),
+             # thin wide views (at most 96 rows, too long for one workgroup):
+             # fp32 A and B; one to many Gram chunks; both sides of 96 rows
+             (33, 777), (777, 33), (1, 5000), (64, 5000), (96, 1000), (97, 1000), (2, 70000), (70000, 40)]
 
 
 @pytest.mark.parametrize("shape", NS_SHAPES)
@@ -263,6 +254,27 @@ def test_muon_step_small_path_edges(mm, dev, dtype, ns_steps):
     check_step(mm, wl, host, devg, ws, hp)
 
 
+# Thin wide views (at most 96 rows, longer than one workgroup holds): the
+# Gram partials / fp32 polynomial / B X launches, tall and wide, one row or
+# column, one or several Gram chunks.
+THIN_SHAPES = ((33, 777), (777, 33), (1, 300), (300, 1), (96, 1000), (64, 2100))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ns_steps", [5, 1])
+def test_muon_step_thin_groups(mm, dev, dtype, ns_steps):
+    """Every stage of one step for thin groups, all in one call next to a
+    tiled group; with ns_steps == 1 the workspace still holds X0."""
+    import torch
+    say(f"[step] thin groups dtype={dtype} ns_steps={ns_steps}")
+    wl = gen.small_workload(THIN_SHAPES + ((300, 520),), batch=2, dtype=dtype)
+    host, devg = make_groups(wl, 31 + ns_steps, dev)
+    hp = mm.HParams(ns_steps=ns_steps)
+    ws = mm.muon_step(devg, hp)
+    torch.cuda.synchronize()
+    check_step(mm, wl, host, devg, ws, hp)
+
+
 def test_muon_step_mixed_contraction_lengths(mm, dev):
     """256-tile groups whose X X^T products differ 4x in contraction length,
     in one launch per stage: problems ordered by contraction length, each
@@ -413,6 +425,70 @@ def test_determinism(mm, dev):
         outs.append([to_host(w) for w, _, _ in devg] + [to_host(m) for _, _, m in devg])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def test_resume_from_saved_state_is_bitwise(mm, dev):
+    """The library keeps no state between calls: ten steps in a row give the
+    same bits as five steps, a save of (W, M) to host memory, a restore into
+    fresh device buffers with a fresh workspace, and five more steps (the
+    optimizer's whole state is the momentum buffer: "MuonClip", section 03;
+    "Muon and MuonClip", "The Muon optimizer").  One tiled, one thin and one
+    single-workgroup group, bf16 parameters, gradients drawn per step."""
+    import torch
+    say("[resume] 10 steps against 5 + save / restore + 5")
+    wl = gen.small_workload(((300, 520), (777, 33), (100, 250)), batch=2, dtype="bf16")
+    hp = mm.HParams()
+    grads = [[to_dev(gen._cast(gen.gaussian(gen.rng(1000 * t + gi), (2, g.rows, g.cols), 1.0), "bf16"), dev)
+              for gi, g in enumerate(wl.groups)] for t in range(10)]
+    host, run_a = make_groups(wl, 41, dev)
+    _, run_b = make_groups(wl, 41, dev)
+    ws = None
+    for t in range(10):
+        ws = mm.muon_step([(W, grads[t][gi], M) for gi, (W, _, M) in enumerate(run_a)], hp, workspace=ws)
+    ws_b = None
+    for t in range(5):
+        ws_b = mm.muon_step([(W, grads[t][gi], M) for gi, (W, _, M) in enumerate(run_b)], hp, workspace=ws_b)
+    torch.cuda.synchronize()
+    saved = [(to_host(W).copy(), to_host(M).copy()) for W, _, M in run_b]
+    del run_b, ws_b
+    torch.cuda.empty_cache()
+    restored = [(to_dev(Wh, dev), to_dev(Mh, dev)) for Wh, Mh in saved]
+    ws_c = None
+    for t in range(5, 10):
+        ws_c = mm.muon_step([(W, grads[t][gi], M) for gi, (W, M) in enumerate(restored)], hp, workspace=ws_c)
+    torch.cuda.synchronize()
+    for gi, ((Wa, _, Ma), (Wc, Mc)) in enumerate(zip(run_a, restored)):
+        dw = int(np.count_nonzero(to_host(Wa) != to_host(Wc)))
+        dm = int(np.count_nonzero(to_host(Ma) != to_host(Mc)))
+        say(f"   group {gi}: differing W elements {dw}, M elements {dm}")
+        assert dw == 0 and dm == 0
+
+
+# The interactive demo of "Muon and MuonClip" ("Newton-Schulz pushing
+# singular values towards 1") spreads its singular values over a condition
+# number of 1000.  Here: full-rank matrices whose singular values sit on 16
+# log-spaced levels from 1 to 1e-3.  After normalisation about a third of
+# them lie below the 0.0015 floor the tuned iteration lifts into its band
+# within five steps; they stay in the region where p(s) ~ a s amplifies the
+# noise of any rounding of X.  The fp64 oracle itself moves by e_in when only
+# its input is rounded to bf16 (the kernel's X0); the GPU result is held to
+# 2e-2 + 1.5 e_in and both numbers are printed.
+@pytest.mark.parametrize("rows,cols", [(512, 2048), (7168, 8192)])
+def test_ns_demo_spectrum(mm, dev, rows, cols):
+    import torch
+    say(f"[ns demo spectrum] {rows}x{cols}, 16 levels 1 .. 1e-3")
+    g = gen.rng(rows + cols)
+    U = gen.with_spectrum(g, rows, cols, gen.log_spaced_levels(min(rows, cols))).astype(np.float32)
+    out = mm.ns_orthogonalize(to_dev(U[None], dev))
+    torch.cuda.synchronize()
+    got = O.bf16_bits_to_f64(to_host(out)[0])
+    del out
+    U64 = U.astype(np.float64)
+    ref = O.newton_schulz(U64)
+    err = rel_fro(got, ref)
+    e_in = rel_fro(O.newton_schulz(O.bf16_bits_to_f64(O.f64_to_bf16_bits(U64))), ref)
+    say(f"   rel err vs oracle {err:.3e}; oracle's own change under a bf16 input {e_in:.3e}")
+    assert err <= 2e-2 + 1.5 * e_in
 
 
 # ---------------------------------------------------------------------------

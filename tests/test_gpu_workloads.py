@@ -154,8 +154,8 @@ def test_workload4_moe_64_experts(mm):
 def test_workload5_muonclip_layer(mm):
     """Workload 5 exactly as the benchmark runs it: per-head S_max on the
     forward's Q, K [4, 4096, 64, 128] (all 64 heads against the oracle), the
-    Muon step on W_q, W_k, W_v [8192x7168] and W_o [7168x8192] (sampled
-    matrices), then the per-head rescale; clip flags bit-exact."""
+    Muon step on W_q, W_k, W_v [8192x7168] and W_o [7168x8192] (every
+    matrix), then the per-head rescale; clip flags bit-exact."""
     import torch
     say("[workload 5] MuonClip layer")
     wl = gen.workload(5)
@@ -206,10 +206,11 @@ def test_workload5_muonclip_layer(mm):
                 assert np.all(np.abs(x - exact) <= bound * (1 + 1e-12))
             else:
                 assert np.array_equal(to_host(devg[0][0][gidx])[rows], Wmid[rows])
-    # sampled Muon matrices: W_v (tall class, never rescaled) and W_o (wide)
-    b = 2
-    check_matrix("W_v", Wqkv[b], Mqkv[b], Gqkv[b], to_host(devg[0][0][b]), to_host(devg[0][2][b]),
-                 O.bf16_bits_to_f64(to_host(o[b])), hp, 8192, 7168, "bf16")
+    # the Muon step of every matrix: W_q and W_k checked on their post-step,
+    # pre-clip weights; W_v (tall class, never rescaled) and W_o (wide)
+    for b, name, Wg in ((0, "W_q", Wq_mid), (1, "W_k", Wk_mid), (2, "W_v", to_host(devg[0][0][2]))):
+        check_matrix(name, Wqkv[b], Mqkv[b], Gqkv[b], Wg, to_host(devg[0][2][b]),
+                     O.bf16_bits_to_f64(to_host(o[b])), hp, 8192, 7168, "bf16")
     o1, _, _ = mm.workspace_views(devg, 1, ws, hp.ns_steps)
     check_matrix("W_o", Wo[0], Mo[0], Go[0], to_host(devg[1][0][0]), to_host(devg[1][2][0]),
                  O.bf16_bits_to_f64(to_host(o1[0])), hp, 7168, 8192, "bf16")
