@@ -177,6 +177,24 @@ int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H,
                   int d_head, float logit_scale, int causal, float* s_max,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ----------------------------------------------------- qkclip_rowmax_noalloc
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * statistic as qkclip_rowmax, same kernels and results bit for bit, with no
+ * workspace argument.  Its partial maxima (B * H * ceil(T / 256) floats) live
+ * in a 1 MiB array inside the library, one per GPU, held until the process
+ * ends; the call allocates nothing.  Limit:
+ *   B * H * ceil(T / 256) <= qkclip_rowmax_noalloc_max_partials() (262144),
+ * else MUON_ERR_WORKSPACE with nothing launched; the other argument errors are
+ * qkclip_rowmax's.  Every call on one GPU shares that array: calls that
+ * overlap in time on one GPU (concurrent streams, or threads) race and must
+ * be serialised by the caller; the array keeps the last call's partials,
+ * and nothing in it needs to start at zero.                                 */
+size_t qkclip_rowmax_noalloc_max_partials(void);
+int qkclip_rowmax_noalloc(const uint16_t* Q, const uint16_t* K, int B, int T,
+                          int H, int d_head, float logit_scale, int causal,
+                          float* s_max, hipStream_t stream);
+
 /* ------------------------------------------------------------------ attn_fwd
  * Softmax attention forward that also produces QK-Clip's statistic, the way
  * the pages place it ([MC] 05: the per-head signal is read off the forward;

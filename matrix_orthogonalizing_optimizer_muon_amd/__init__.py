@@ -99,6 +99,10 @@ def load_library() -> ctypes.CDLL:
     lib.qkclip_rowmax_workspace_size.restype = sz
     lib.qkclip_rowmax.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, sz, vp]
     lib.qkclip_rowmax.restype = i32
+    lib.qkclip_rowmax_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.qkclip_rowmax_noalloc.restype = i32
+    lib.qkclip_rowmax_noalloc_max_partials.argtypes = []
+    lib.qkclip_rowmax_noalloc_max_partials.restype = sz
     lib.qkclip_rescale.argtypes = [vp, vp, i32, i32, i32, i32, vp, f32, f32, vp, vp]
     lib.qkclip_rescale.restype = i32
     lib.qkclip_rescale_slices.argtypes = [ctypes.POINTER(_Slice), i32, i32, i32, vp, f32, vp, vp]
@@ -324,6 +328,28 @@ def qkclip_rowmax(Q, K, logit_scale: float | None = None, causal: bool = True, o
     _check(lib.qkclip_rowmax(Q.data_ptr(), K.data_ptr(), B, T, H, D, logit_scale, int(bool(causal)),
                              out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
            "qkclip_rowmax")
+    return out
+
+
+def qkclip_rowmax_noalloc(Q, K, logit_scale: float | None = None, causal: bool = True, out=None):
+    """qkclip_rowmax without a workspace: the library's own per-GPU scratch
+    holds the partial maxima (B * H * ceil(T / 256) of them, at most
+    qkclip_rowmax_noalloc_max_partials()).  Calls that overlap on one GPU
+    race.  Returns fp32 [H]."""
+    torch = _torch()
+    lib = load_library()
+    _need_cuda(Q, K)
+    if Q.dtype != torch.bfloat16 or K.dtype != torch.bfloat16:
+        raise TypeError("Q and K must be bfloat16")
+    if Q.dim() != 4 or Q.shape != K.shape or not Q.is_contiguous() or not K.is_contiguous():
+        raise ValueError("Q and K must be contiguous [B, T, H, d_head] tensors of one shape")
+    B, T, H, D = Q.shape
+    if logit_scale is None:
+        logit_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty(H, dtype=torch.float32, device=Q.device)
+    _check(lib.qkclip_rowmax_noalloc(Q.data_ptr(), K.data_ptr(), B, T, H, D, logit_scale, int(bool(causal)),
+                                     out.data_ptr(), _stream()), "qkclip_rowmax_noalloc")
     return out
 
 

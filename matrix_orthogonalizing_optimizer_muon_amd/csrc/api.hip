@@ -669,18 +669,53 @@ size_t qkclip_rowmax_workspace_size(int B, int T, int H) {
   return align_up(static_cast<size_t>(B) * H * nqb * sizeof(float));
 }
 
-int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int d_head, float logit_scale,
-                  int causal, float* s_max, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the two row-max entry points; nqb receives the
+// number of 256-query blocks per (batch row, head).
+int rowmax_args(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int d_head, float logit_scale,
+                const float* s_max, int* nqb) {
   if (!Q || !K || !s_max || B < 1 || T < 1 || H < 1 || d_head < 1) return MUON_ERR_INVALID_ARG;
   if (!(logit_scale > 0.0f) || !isfinite(logit_scale)) return MUON_ERR_INVALID_ARG;
   if (d_head != 64 && d_head != 128 && d_head != 256) return MUON_ERR_UNSUPPORTED;
   if (!aligned(Q, 16) || !aligned(K, 16)) return MUON_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * T * H * d_head > (int64_t(1) << 40)) return MUON_ERR_INVALID_ARG;
-  const int nqb = (T + 255) / 256;   // query blocks of the row-max kernel
-  if (static_cast<int64_t>(B) * H * nqb > (int64_t(1) << 31) - 1) return MUON_ERR_INVALID_ARG;
+  *nqb = (T + 255) / 256;   // query blocks of the row-max kernel
+  if (static_cast<int64_t>(B) * H * *nqb > (int64_t(1) << 31) - 1) return MUON_ERR_INVALID_ARG;
+  return MUON_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int d_head, float logit_scale,
+                  int causal, float* s_max, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int nqb = 0;
+  const int st = rowmax_args(Q, K, B, T, H, d_head, logit_scale, s_max, &nqb);
+  if (st != MUON_OK) return st;
   const size_t need = qkclip_rowmax_workspace_size(B, T, H);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return MUON_ERR_WORKSPACE;
   float* partial = static_cast<float*>(workspace);
+  MUON_LAUNCH(KIND_QK_ROWMAX, stream,
+              launch_qk_rowmax(reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K), B, T, H,
+                               d_head, causal ? 1 : 0, partial, nqb, stream));
+  MUON_LAUNCH(KIND_QK_REDUCE, stream, launch_qk_reduce(partial, B, H, nqb, logit_scale, s_max, stream));
+  return MUON_OK;
+}
+
+size_t qkclip_rowmax_noalloc_max_partials(void) { return static_cast<size_t>(kNoAllocPartials); }
+
+int qkclip_rowmax_noalloc(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int d_head, float logit_scale,
+                          int causal, float* s_max, hipStream_t stream) {
+  int nqb = 0;
+  const int st = rowmax_args(Q, K, B, T, H, d_head, logit_scale, s_max, &nqb);
+  if (st != MUON_OK) return st;
+  if (static_cast<int64_t>(B) * H * nqb > kNoAllocPartials) return MUON_ERR_WORKSPACE;
+  float* partial = nullptr;
+  if (noalloc_partials(&partial) != hipSuccess) return MUON_ERR_HIP;
+  // every partial the reduction reads is written by its row-max block first,
+  // so the scratch needs no clearing between calls
   MUON_LAUNCH(KIND_QK_ROWMAX, stream,
               launch_qk_rowmax(reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K), B, T, H,
                                d_head, causal ? 1 : 0, partial, nqb, stream));

@@ -303,6 +303,12 @@ hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int 
                             int causal, float* partial, int nqb, hipStream_t s);
 hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float logit_scale,
                             float* s_max, hipStream_t s);
+// qkclip_rowmax_noalloc: its partial maxima live in a file-scope __device__
+// array of kNoAllocPartials floats (qkclip.hip); noalloc_partials gives that
+// array's address on the current device (looked up once per device).
+constexpr int kNoAllocPartials = 1 << 18;   // 1 MiB
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_partials(float** out);
 // Per-head row rescale of up to kMaxRescaleSlices row slices: head h owns
 // rows [h * head_pitch, h * head_pitch + rows_per_head) of m[z].W (cols
 // elements per row), scaled by gamma^expo.

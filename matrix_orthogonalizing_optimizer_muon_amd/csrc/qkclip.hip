@@ -15,10 +15,36 @@
 // cross-lane max, across the block through LDS, and across blocks by a
 // second, fixed-order kernel (no atomics, no initialisation pass).
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
+// Scratch of qkclip_rowmax_noalloc: the row-max pass's per-block partial
+// maxima, for callers that cannot allocate.  Each GPU the library runs on
+// holds its own copy until the process ends.  Host code never uses this name
+// as an address (on the host it is a stand-in, not device memory): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[muon::kNoAllocPartials];
+
 namespace muon {
+
+hipError_t noalloc_partials(float** out) {
+  static std::mutex mu;
+  static float* ptrs[kMaxDevices] = {nullptr};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = static_cast<float*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -224,6 +224,19 @@ static void qkclip_and_friends() {
     CHECK(qkclip_rowmax(q, k, B, T, H, d, 0.125f, 1, s, w, ws, nullptr) == MUON_OK);
   }
   {
+    // the no-allocation variant: within its 262144 partials, and one past
+    const uint16_t* q = static_cast<const uint16_t*>(fake(uint64_t(4) * 4096 * 64 * 128 * 2));
+    float* s = static_cast<float*>(fake(64 * 4));
+    CHECK(qkclip_rowmax_noalloc_max_partials() == 262144);
+    const long before = stub_launches();
+    CHECK(qkclip_rowmax_noalloc(q, q, 4, 4096, 64, 128, 0.088f, 1, s, nullptr) == MUON_OK);
+    CHECK(stub_launches() == before + 2);
+    CHECK(qkclip_rowmax_noalloc(q, q, 1, 256 * 4097, 64, 64, 0.125f, 1, s, nullptr) == MUON_ERR_WORKSPACE);
+    CHECK(qkclip_rowmax_noalloc(q, q, 1, 16, 2, 96, 0.1f, 1, s, nullptr) == MUON_ERR_UNSUPPORTED);
+    CHECK(qkclip_rowmax_noalloc(nullptr, q, 1, 16, 2, 64, 0.1f, 1, s, nullptr) == MUON_ERR_INVALID_ARG);
+    CHECK(stub_launches() == before + 2);
+  }
+  {
     const uint64_t n = uint64_t(B) * T * H * 128;
     const uint16_t* q = static_cast<const uint16_t*>(fake(n * 2));
     uint16_t* o = static_cast<uint16_t*>(fake(n * 2));

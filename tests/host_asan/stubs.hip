@@ -330,6 +330,15 @@ hipError_t launch_dion_colnorm(const DionArgs& A, int batch, hipStream_t) {
   return hipSuccess;
 }
 
+// the no-allocation row-max's scratch: a fixed address range, registered on
+// each lookup (the real one is a __device__ array found by symbol)
+hipError_t noalloc_partials(float** out) {
+  const uintptr_t base = uintptr_t(0x7000) << 32;
+  stub_register(reinterpret_cast<void*>(base), uint64_t(kNoAllocPartials) * 4);
+  *out = reinterpret_cast<float*>(base);
+  return hipSuccess;
+}
+
 hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t) {
   ++g_launches;
   if (blocks < 1 || iters < 1) fail("probe grid");
