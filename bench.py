@@ -59,6 +59,11 @@ def parse():
     ap.add_argument("--summarize-profile", nargs="+", metavar="CSV",
                     help="print a per-kernel summary of rocprofv3 kernel-trace or counter CSV "
                          "files and exit (no GPU use)")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs, "
+                         "scaled by the same counters of the 1 GiB copy (--copy-calibration); "
+                         "prints a table and a TRAFFIC_JSON line, then exits (no GPU use)")
     return ap.parse_args()
 
 
@@ -116,6 +121,9 @@ def main():
     args = parse()
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -770,6 +778,56 @@ def summarize_profile(paths):
             print(f"# {'kernel':28s} {'counter':>12s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
             for (k, c), v in sorted(d.items()):
                 print(f"  {k:28s} {c:>12s} {len(v):10d} {sum(v) / len(v):18.1f}")
+
+
+KERNEL_SOURCES = {
+    "ns_": "ns_gemm.hip", "momentum_norm": "elementwise.hip", "param_update": "elementwise.hip",
+    "qk_": "qkclip.hip", "small_step": "small.hip", "ns_thin": "thin.hip", "adamw": "adamw.hip",
+    "attn_fwd": "attention.hip"}
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes=1 << 30):
+    """HBM read and write bytes per launch of each of the library's kernels.
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled so that the plain
+    1 GiB device copy reads and writes 1 GiB: read = f_r x FETCH_SIZE,
+    write = f_w x WRITE_SIZE.  Kernels outside the library are left out."""
+    import csv
+    import hashlib
+    from collections import defaultdict
+
+    def per_kernel(path):
+        d = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            d[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024.0)
+        return d
+
+    def copy_value(path):
+        vals = [float(r["Counter_Value"]) * 1024.0 for r in csv.DictReader(open(path))
+                if "copy" in r["Kernel_Name"].lower()]
+        return sum(vals) / len(vals)
+
+    f_r = copy_bytes / copy_value(copy_fetch_csv)
+    f_w = copy_bytes / copy_value(copy_write_csv)
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    print(f"# copy of {copy_bytes / 2**30:.0f} GiB: read bytes = {f_r:.3f} x FETCH_SIZE, "
+          f"write bytes = {f_w:.3f} x WRITE_SIZE")
+    print(f"# {'kernel':28s} {'launches':>8s} {'read_GB':>9s} {'write_GB':>9s} {'total_GB':>9s}  (mean per launch)")
+    out = {}
+    for k in sorted(fetch):
+        if k.startswith("(other") or k not in write:
+            continue
+        rd = f_r * sum(fetch[k]) / len(fetch[k])
+        wr = f_w * sum(write[k]) / len(write[k])
+        print(f"  {k:28s} {len(fetch[k]):8d} {rd / 1e9:9.3f} {wr / 1e9:9.3f} {(rd + wr) / 1e9:9.3f}")
+        src = next((v for pfx, v in KERNEL_SOURCES.items() if k.startswith(pfx)), None)
+        rel = os.path.join("matrix_orthogonalizing_optimizer_muon_amd", "csrc", src) if src else None
+        sha = (hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()[:16]
+               if rel and os.path.exists(os.path.join(ROOT, rel)) else None)
+        out[k] = {"read_bytes": rd, "write_bytes": wr, "total_bytes": rd + wr, "source": rel,
+                  "source_sha256_16": sha}
+    print("#")
+    print("# machine-readable (bench.py uses an entry only while its source hash matches):")
+    print("TRAFFIC_JSON " + json.dumps(out, sort_keys=True))
 
 
 if __name__ == "__main__":
