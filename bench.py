@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--summarize-profile", nargs="+", metavar="CSV",
                     help="print a per-kernel summary of rocprofv3 kernel-trace or counter CSV "
                          "files and exit (no GPU use)")
+    ap.add_argument("--summarize-clock", nargs="+", metavar="CSV",
+                    help="print each kernel's shader clock and MFMA busy share from rocprofv3 counter "
+                         "CSVs of GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES and exit (no GPU use)")
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs, "
@@ -125,6 +128,9 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    "(the step shards by whole matrices across GPUs, which is not built here)",
@@ -149,13 +155,14 @@ def main():
         print(json.dumps(res), flush=True)
         return
 
-    peak = None if args.headline_only else mfma_peak(mm, torch, dev)
-    if peak:
-        note(f"register-only MFMA loop: {peak['tflops']} TFLOP/s")
-
     # ---------------- headline: the 24-layer decoder's Muon group
     head = muon_config_run(mm, torch, dev, seed, 3, args.steps, args.warmup, roofline=True)
     note("24-layer decoder step timed")
+    # the matrix-core probe runs after the headline, on a GPU already at its working clock
+    peak = None if args.headline_only else mfma_peak(mm, torch, dev)
+    if peak:
+        note(f"register-only MFMA loop: {peak['tflops']} TFLOP/s on random operands, "
+             f"{peak['smooth_operands_tflops']} on smooth ones")
     out = {
         "metric": "Muon steps/s + Newton–Schulz TFLOP/s (% bf16 MFMA peak), 1 MI355X",
         "value": head["steps_per_s"],
@@ -204,26 +211,36 @@ def main():
 # readings
 # ---------------------------------------------------------------------------
 
-def mfma_peak(mm, torch, dev, iters=20000):
+def mfma_peak(mm, torch, dev, iters=8000):
     """The register-only MFMA loop on every CU (two 256-thread blocks per CU,
-    one wave per SIMD each), timed with events: the sustained bf16 matrix-core
-    rate at the clock the chip holds under that load."""
+    one wave per SIMD each, eight accumulators per wave), timed with events:
+    the sustained bf16 matrix-core rate at the clock the chip holds under that
+    load.  The matrix cores draw more power, and the chip holds a lower clock,
+    on random operands than on smooth ones; the random-operand rate is the one
+    the Newton-Schulz products are compared with (their operands are
+    random-like).  About 80 ms of warm-up, then the best of 3 runs per kind."""
     ncu = torch.cuda.get_device_properties(dev).multi_processor_count
     blocks = 2 * ncu
     sink = torch.empty(blocks, dtype=torch.float32, device=dev)
-    mm.mfma_probe(blocks, 200, sink)
+    for _ in range(8):
+        mm.mfma_probe(blocks, iters, sink, mm.PROBE_RANDOM)
     torch.cuda.synchronize()
-    best = 0.0
-    for _ in range(3):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        flop = mm.mfma_probe(blocks, iters, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
-    return {"tflops": round(best, 1), "frac_of_spec": round(best / MFMA_BF16_PEAK_TFLOPS, 4),
-            "probe": f"{blocks} blocks x 4 waves x 4 x {iters} v_mfma_f32_32x32x16_bf16, best of 3"}
+    best = {}
+    for kind in (mm.PROBE_RANDOM, mm.PROBE_SMOOTH):
+        best[kind] = 0.0
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            flop = mm.mfma_probe(blocks, iters, sink, kind)
+            e1.record()
+            torch.cuda.synchronize()
+            best[kind] = max(best[kind], flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    r = best[mm.PROBE_RANDOM]
+    return {"tflops": round(r, 1), "frac_of_spec": round(r / MFMA_BF16_PEAK_TFLOPS, 4),
+            "smooth_operands_tflops": round(best[mm.PROBE_SMOOTH], 1),
+            "probe": f"{blocks} blocks x 4 waves x 32 x {iters} v_mfma_f32_32x32x16_bf16 on random bf16 "
+                     "register operands (smooth operands beside it), best of 3 after ~80 ms of warm-up"}
 
 
 def make_config_groups(mm, torch, dev, seed, idx):
@@ -778,6 +795,45 @@ def summarize_profile(paths):
             print(f"# {'kernel':28s} {'counter':>12s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
             for (k, c), v in sorted(d.items()):
                 print(f"  {k:28s} {c:>12s} {len(v):10d} {sum(v) / len(v):18.1f}")
+
+
+def summarize_clock(paths, flops=None):
+    """Per-kernel shader clock and MFMA activity from a rocprofv3 counter
+    collection of GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES (one run).
+    GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles, so the clock is
+    GRBM / 8 / duration; SQ_VALU_MFMA_BUSY_CYCLES counts busy cycles of the
+    1024 SIMDs' matrix pipes in units of 8 SIMD-cycles per GRBM cycle summed
+    the same way, so the busy share of the matrix pipes is
+    MFMA_BUSY / GRBM / 128 (checked against the algorithmic flop of the
+    Newton-Schulz products: flop / duration / (clock x 1024 flop/clk x 1024))."""
+    import csv
+    import statistics
+    from collections import defaultdict
+    for path in paths:
+        per = defaultdict(dict)
+        for r in csv.DictReader(open(path)):
+            key = (short_name(r["Kernel_Name"]), r["Kernel_Name"][:200], r["Dispatch_Id"])
+            per[key][r["Counter_Name"]] = float(r["Counter_Value"])
+            per[key]["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        groups = defaultdict(list)
+        for (k, full, _), v in per.items():
+            if "GRBM_GUI_ACTIVE" in v and "SQ_VALU_MFMA_BUSY_CYCLES" in v and v["dur"] > 0:
+                groups[(k, full)].append(v)
+        print(f"# {os.path.basename(path)}")
+        print(f"# {'kernel':28s} {'launches':>8s} {'median_us':>10s} {'clock_GHz':>10s} {'mfma_busy_%':>12s}")
+        for (k, full), vs in sorted(groups.items(), key=lambda kv: -sum(v["dur"] for v in kv[1])):
+            if k.startswith("(other"):
+                continue
+            tag = k
+            if k.startswith("ns_") and "<256, 128" in full:
+                tag = k + "_slices" if not k.endswith("_slices") else k
+            clk = statistics.median(v["GRBM_GUI_ACTIVE"] / 8 / v["dur"] / 1e9 for v in vs)
+            busy = statistics.median(v["SQ_VALU_MFMA_BUSY_CYCLES"] / v["GRBM_GUI_ACTIVE"] / 128 * 100 for v in vs)
+            dur = statistics.median(v["dur"] for v in vs) * 1e6
+            if dur < 50.0:   # the counters' window is longer than a short kernel
+                print(f"  {tag:28s} {len(vs):8d} {dur:10.1f} {'-':>10s} {'-':>12s}")
+            else:
+                print(f"  {tag:28s} {len(vs):8d} {dur:10.1f} {clk:10.3f} {busy:12.1f}")
 
 
 KERNEL_SOURCES = {

@@ -322,13 +322,20 @@ int dion_step(void* param, int dtype, const void* grad, float* momentum, float* 
 const char* muon_status_string(int status);
 
 /* Matrix-core rate probe (not part of the optimizer): `blocks` workgroups of
- * 256 threads, each wave issuing 4 * iters v_mfma_f32_32x32x16_bf16 on
- * register operands, no memory traffic in the loop; 32768 flop per MFMA, so
- * blocks * 4 * 4 * iters * 32768 flop per launch.  Time it with events on
- * `stream` to get the sustained bf16 MFMA rate at the clock the chip holds
- * under that load.  sink: device float[blocks], written once per block.
- * MUON_ERR_INVALID_ARG for blocks outside 1..2^20, iters < 1 or a null sink. */
-int muon_mfma_probe(int blocks, int iters, float* sink, hipStream_t stream);
+ * 256 threads, each wave issuing 32 * iters v_mfma_f32_32x32x16_bf16 on
+ * register operands (eight independent accumulators), no memory traffic in
+ * the loop; 32768 flop per MFMA, so blocks * 4 * 32 * iters * 32768 flop per
+ * launch.  Time it with events on `stream` to get the sustained bf16 MFMA rate
+ * at the clock the chip holds under that load.  The matrix cores draw more
+ * power on random operands than on smooth ones, so the rate depends on the
+ * operand kind: MUON_PROBE_RANDOM (pseudo-random bf16 of both signs, like the
+ * Newton-Schulz iterates) or MUON_PROBE_SMOOTH (small positive values that
+ * vary slowly across lanes).  sink: device float[blocks], written once per
+ * block.  MUON_ERR_INVALID_ARG for blocks outside 1..2^20, iters outside
+ * 1..2^24, an unknown operand kind or a null sink. */
+#define MUON_PROBE_RANDOM 0
+#define MUON_PROBE_SMOOTH 1
+int muon_mfma_probe(int blocks, int iters, int operands, float* sink, hipStream_t stream);
 
 /* Optional per-kernel timing with HIP events recorded around every launch
  * the library makes on the caller's stream.  muon_profile_enable(1) clears

@@ -119,7 +119,7 @@ def load_library() -> ctypes.CDLL:
     lib.dion_step.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i64, f32, f32, vp, sz, vp]
     lib.dion_step.restype = i32
     lib.adamw_step.restype = i32
-    lib.muon_mfma_probe.argtypes = [i32, i32, vp, vp]
+    lib.muon_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
     lib.muon_mfma_probe.restype = i32
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
@@ -535,15 +535,20 @@ def dion_step(param, grad, momentum, q, *, lr: float, mu: float = 0.95, workspac
     return workspace
 
 
-def mfma_probe(blocks: int, iters: int, sink):
+PROBE_RANDOM = 0
+PROBE_SMOOTH = 1
+
+
+def mfma_probe(blocks: int, iters: int, sink, operands: int = PROBE_RANDOM):
     """Launch the register-only bf16 MFMA loop on the current stream (see
-    muon_mfma_probe); sink: a float32 device tensor of >= blocks elements.
-    Returns the launch's flop count."""
+    muon_mfma_probe); sink: a float32 device tensor of >= blocks elements;
+    operands: PROBE_RANDOM or PROBE_SMOOTH.  Returns the launch's flop count."""
     _need_cuda(sink)
     if sink.dtype != _torch().float32 or sink.numel() < blocks:
         raise ValueError("sink must be a float32 tensor of at least `blocks` elements")
-    _check(load_library().muon_mfma_probe(blocks, iters, sink.data_ptr(), _stream()), "muon_mfma_probe")
-    return blocks * 4 * 4 * iters * 32768
+    _check(load_library().muon_mfma_probe(blocks, iters, int(operands), sink.data_ptr(), _stream()),
+           "muon_mfma_probe")
+    return blocks * 4 * 32 * iters * 32768
 
 
 def profile_enable(on: bool = True):

@@ -975,9 +975,10 @@ int dion_step(void* param, int dtype, const void* grad, float* momentum, float* 
   return MUON_OK;
 }
 
-int muon_mfma_probe(int blocks, int iters, float* sink, hipStream_t stream) {
-  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || !sink) return MUON_ERR_INVALID_ARG;
-  if (launch_mfma_probe(blocks, iters, sink, stream) != hipSuccess) return MUON_ERR_HIP;
+int muon_mfma_probe(int blocks, int iters, int operands, float* sink, hipStream_t stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24) || !sink) return MUON_ERR_INVALID_ARG;
+  if (operands != MUON_PROBE_RANDOM && operands != MUON_PROBE_SMOOTH) return MUON_ERR_INVALID_ARG;
+  if (launch_mfma_probe(blocks, iters, operands, sink, stream) != hipSuccess) return MUON_ERR_HIP;
   return MUON_OK;
 }
 

@@ -206,8 +206,10 @@ static void invalid_arguments() {
   CHECK(dion_step(W, 1, W, qd, qd, 1, 64, 64, 16, 4096, 0.02f, 0.95f, w, 8, nullptr) == MUON_ERR_WORKSPACE);
   CHECK(dion_step(nullptr, 1, W, qd, qd, 1, 64, 64, 16, 4096, 0.02f, 0.95f, w, 1 << 20, nullptr) == MUON_ERR_INVALID_ARG);
   // probe
-  CHECK(muon_mfma_probe(0, 1, s, nullptr) == MUON_ERR_INVALID_ARG);
-  CHECK(muon_mfma_probe(1, 1, nullptr, nullptr) == MUON_ERR_INVALID_ARG);
+  CHECK(muon_mfma_probe(0, 1, MUON_PROBE_RANDOM, s, nullptr) == MUON_ERR_INVALID_ARG);
+  CHECK(muon_mfma_probe(1, 1, MUON_PROBE_RANDOM, nullptr, nullptr) == MUON_ERR_INVALID_ARG);
+  CHECK(muon_mfma_probe(1, 1, 2, s, nullptr) == MUON_ERR_INVALID_ARG);
+  CHECK(muon_mfma_probe(1, (1 << 24) + 1, MUON_PROBE_SMOOTH, s, nullptr) == MUON_ERR_INVALID_ARG);
   for (int k = 0; k < 5; ++k) CHECK(muon_status_string(k) && strlen(muon_status_string(k)) > 0);
   CHECK(stub_launches() == 0);
 }
@@ -287,13 +289,14 @@ static void qkclip_and_friends() {
   }
   {
     float* sink = static_cast<float*>(fake(512 * 4));
-    CHECK(muon_mfma_probe(512, 10, sink, nullptr) == MUON_OK);
+    CHECK(muon_mfma_probe(512, 10, MUON_PROBE_RANDOM, sink, nullptr) == MUON_OK);
+    CHECK(muon_mfma_probe(512, 10, MUON_PROBE_SMOOTH, sink, nullptr) == MUON_OK);
   }
   // the profiler: on, one call, collect, off
   CHECK(muon_profile_enable(1) == MUON_OK);
   {
     float* sink = static_cast<float*>(fake(4));
-    CHECK(muon_mfma_probe(1, 1, sink, nullptr) == MUON_OK);
+    CHECK(muon_mfma_probe(1, 1, MUON_PROBE_RANDOM, sink, nullptr) == MUON_OK);
   }
   double ms[64];
   int64_t cnt[64];

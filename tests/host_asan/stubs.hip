@@ -339,9 +339,9 @@ hipError_t noalloc_partials(float** out) {
   return hipSuccess;
 }
 
-hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t) {
+hipError_t launch_mfma_probe(int blocks, int iters, int operands, float* sink, hipStream_t) {
   ++g_launches;
-  if (blocks < 1 || iters < 1) fail("probe grid");
+  if (blocks < 1 || iters < 1 || (operands != MUON_PROBE_RANDOM && operands != MUON_PROBE_SMOOTH)) fail("probe args");
   need(sink, static_cast<uint64_t>(blocks) * 4, "probe sink");
   return hipSuccess;
 }
