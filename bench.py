@@ -425,9 +425,11 @@ def muonclip_layer_reading(mm, torch, dev, seed, steps, warmup, companions=False
         kern["qk_rowmax"]["frac_mfma_peak"] = round(qk_flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
         kern["qk_rowmax"]["bytes_read"] = 2 * B * T * H * D * 2
     if prof["qk_reduce"][1]:
-        # per-head reduction of the row-max pass's partial maxima: B H ceil(T / 256)
-        # fp32 partials read, H fp32 written; launch-bound at this size
-        by = 4 * (B * H * ((T + 255) // 256) + H)
+        # per-head reduction of the row-max pass's partial maxima: B H ceil(T / q)
+        # fp32 partials read (q = 512 queries per block for d = 128, else 256),
+        # H fp32 written; launch-bound at this size
+        q = 512 if D == 128 else 256
+        by = 4 * (B * H * ((T + q - 1) // q) + H)
         t = prof["qk_reduce"][0] / prof["qk_reduce"][1] * 1e-3
         kern["qk_reduce"]["bytes"] = by
         kern["qk_reduce"]["GBs"] = round(by / t / 1e9, 2)

@@ -181,10 +181,11 @@ int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H,
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * statistic as qkclip_rowmax, same kernels and results bit for bit, with no
- * workspace argument.  Its partial maxima (B * H * ceil(T / 256) floats) live
- * in a 1 MiB array inside the library, one per GPU, held until the process
- * ends; the call allocates nothing.  Limit:
- *   B * H * ceil(T / 256) <= qkclip_rowmax_noalloc_max_partials() (262144),
+ * workspace argument.  Its partial maxima (B * H * ceil(T / q) floats, with
+ * q = 512 queries per block for d_head = 128 and 256 otherwise) live in a
+ * 1 MiB array inside the library, one per GPU, held until the process ends;
+ * the call allocates nothing.  Limit:
+ *   B * H * ceil(T / q) <= qkclip_rowmax_noalloc_max_partials() (262144),
  * else MUON_ERR_WORKSPACE with nothing launched; the other argument errors are
  * qkclip_rowmax's.  Every call on one GPU shares that array: calls that
  * overlap in time on one GPU (concurrent streams, or threads) race and must

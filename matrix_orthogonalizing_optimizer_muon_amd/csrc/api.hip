@@ -665,7 +665,7 @@ int ns_orthogonalize(const void* in, int in_dtype, uint16_t* out, int batch, int
 
 size_t qkclip_rowmax_workspace_size(int B, int T, int H) {
   if (B < 1 || T < 1 || H < 1) return 0;
-  const int nqb = (T + 255) / 256;   // query blocks of the row-max kernel
+  const int nqb = (T + 255) / 256;   // the most query blocks of any head dimension (256 queries each)
   return align_up(static_cast<size_t>(B) * H * nqb * sizeof(float));
 }
 
@@ -673,7 +673,7 @@ size_t qkclip_rowmax_workspace_size(int B, int T, int H) {
 
 namespace {
 // Argument checks shared by the two row-max entry points; nqb receives the
-// number of 256-query blocks per (batch row, head).
+// number of query blocks per (batch row, head) of the row-max kernel.
 int rowmax_args(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int d_head, float logit_scale,
                 const float* s_max, int* nqb) {
   if (!Q || !K || !s_max || B < 1 || T < 1 || H < 1 || d_head < 1) return MUON_ERR_INVALID_ARG;
@@ -681,7 +681,8 @@ int rowmax_args(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int d
   if (d_head != 64 && d_head != 128 && d_head != 256) return MUON_ERR_UNSUPPORTED;
   if (!aligned(Q, 16) || !aligned(K, 16)) return MUON_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * T * H * d_head > (int64_t(1) << 40)) return MUON_ERR_INVALID_ARG;
-  *nqb = (T + 255) / 256;   // query blocks of the row-max kernel
+  const int qblk = qk_rowmax_query_block(d_head);
+  *nqb = (T + qblk - 1) / qblk;   // query blocks of the row-max kernel
   if (static_cast<int64_t>(B) * H * *nqb > (int64_t(1) << 31) - 1) return MUON_ERR_INVALID_ARG;
   return MUON_OK;
 }

@@ -299,6 +299,9 @@ hipError_t launch_dion_gram(const DionArgs& A, int batch, hipStream_t s);
 hipError_t launch_dion_gram_reduce(const DionArgs& A, int batch, hipStream_t s);
 hipError_t launch_dion_chol(const DionArgs& A, int batch, hipStream_t s);
 hipError_t launch_dion_colnorm(const DionArgs& A, int batch, hipStream_t s);
+// Queries per block of the row-max kernel for a head dimension (the partial
+// maxima it writes number B * H * ceil(T / that)).
+inline int qk_rowmax_query_block(int d_head) { return d_head == 128 ? 512 : 256; }
 hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int H, int d_head,
                             int causal, float* partial, int nqb, hipStream_t s);
 hipError_t launch_qk_reduce(const float* partial, int B, int H, int nqb, float logit_scale,

@@ -9,11 +9,15 @@
 // balanced rescale; "About Muon: Muon At Scale", "When Softmax Collapses").
 //
 // The statistic is a causal Q K^T contraction reduced by max, so it runs as
-// a flash-style MFMA loop: one block per (batch row, head, 256 queries), the
-// queries' fragments held in registers, 64-key blocks (128 for d = 64)
-// staged through LDS, the logits never stored.  Maxima are reduced across the wavefront with
-// cross-lane max, across the block through LDS, and across blocks by a
-// second, fixed-order kernel (no atomics, no initialisation pass).
+// a flash-style MFMA loop: one block per (batch row, head, 512 queries for
+// d = 128, 256 otherwise), the queries' fragments held in registers, 64-key
+// blocks (128 for d = 64) staged through LDS, the logits never stored.
+// Maxima are reduced across the wavefront with cross-lane max, across the
+// block through LDS, and across blocks by a second, fixed-order kernel (no
+// atomics, no initialisation pass).  Blocks are numbered heaviest query block
+// first across all (batch row, head) pairs: the dispatcher hands them out in
+// that order, so the long causal rows start first on every CU and the short
+// ones fill the end.
 #include <algorithm>
 #include <mutex>
 
@@ -58,12 +62,10 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// One block = 256 consecutive queries of one (batch row, head); 4 waves of
-// 64 query rows, one per SIMD, and two blocks per CU: their barriers are
-// independent, so one block's MFMAs run while the other stages keys or
-// waits (8-wave blocks of 512 queries, two waves per SIMD in one block, took
-// 16% longer: both waves of a SIMD reached each barrier together and left its
-// MFMA pipe idle while the keys were staged).  The queries' fragments stay in registers for
+// d = 64 and 256: one block = 256 consecutive queries of one (batch row,
+// head); 4 waves of 64 query rows, one per SIMD, and two blocks per CU: their
+// barriers are independent, so one block's MFMAs run while the other stages
+// keys or waits.  The queries' fragments stay in registers for
 // the whole key sweep; KB keys at a time are staged through double-buffered
 // LDS (registers one stage ahead, barrier without the workgroup fence so the
 // prefetch stays in flight).  Logits are reduced by max in registers; only
@@ -84,9 +86,9 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   __shared__ float wmax[kWaves];
   __shared__ int wnan[kWaves];
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / nqb;
-  const int qb = nqb - 1 - (lin - bh * nqb);  // heaviest query blocks first
+  const int nbh = B * H;
+  const int bh = blockIdx.x % nbh;
+  const int qb = nqb - 1 - blockIdx.x / nbh;  // heaviest query blocks first
   const int b = bh / H, h = bh - b * H;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -225,6 +227,203 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   }
 }
 
+// d = 128: one block per (batch row, head, 512 queries), 8 waves of 64
+// query rows, two per SIMD.  Waves 0-3 (group 0) and 4-7 (group 1) sit one per
+// SIMD each and take turns: while one group runs its 32 MFMAs of a 64-key
+// stage on register fragments, the other reduces its previous stage's logits
+// by max, reads the next stage's key fragments from LDS and stages its half
+// of a later key block; a barrier separates the turns, so each SIMD always has
+// a wave issuing MFMAs.  Group g stages rows 32g..32g+31 of each key block,
+// two blocks ahead through registers; wave rows interleave between the groups
+// (row offset (2 slot + g) 64) so both reach the causal diagonal together.
+// One block per CU (the 256 registers of two waves per SIMD).  A turn takes
+// about 1.25x its 32 MFMAs of matrix-pipe time; the 4-wave form below, two
+// blocks per CU with independent barriers, leaves the pipes idle more often.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qk_rowmax_pp_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, int B, int T, int H,
+                         int causal, float* __restrict__ partial, int nqb) {
+  constexpr int D = 128, KB = 64, NB = 2, PITCH = D + 8, KS = D / 16, QB = 512;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KB * PITCH];
+  __shared__ float wmax[8];
+  __shared__ int wnan[8];
+
+  const int nbh = B * H;
+  const int bh = blockIdx.x % nbh;
+  const int qb = nqb - 1 - blockIdx.x / nbh;  // heaviest query blocks first
+  const int b = bh / H, h = bh - b * H;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, slot = wave & 3;
+  const int64_t row_stride = static_cast<int64_t>(H) * D;
+  const bf16_t* Qb = Q + static_cast<int64_t>(b) * T * row_stride + static_cast<int64_t>(h) * D;
+  const bf16_t* Kb = K + static_cast<int64_t>(b) * T * row_stride + static_cast<int64_t>(h) * D;
+  const int r0 = qb * QB + (2 * slot + grp) * 64;  // first query row of this wave
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+
+  bf16x8_t qf[2][KS];
+  static_for<2>([&](auto a) {
+    const int row = min(r0 + a * 32 + frow, T - 1);
+    static_for<KS>([&](auto s) {
+      qf[a][s] = *reinterpret_cast<const bf16x8_t*>(Qb + row * row_stride + s * 16 + fk);
+    });
+  });
+
+  const int kend = causal ? min(T, (qb + 1) * QB) : T;
+  const int nkb = (kend + KB - 1) / KB;
+
+  // staging: group g copies rows 32 g + (gt / 16) + 16 c, 16-byte chunk gt % 16
+  const int gt = tid & 255;
+  const int srow = 32 * grp + (gt >> 4), scol = (gt & 15) * 8;
+  u32x4_t rk[2][2];   // [register set][chunk]
+  auto gload = [&](int kb, auto set) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set)::value;
+    const int k0 = min(kb, nkb - 1) * KB;
+    static_for<2>([&](auto c) {
+      const int j = min(k0 + srow + 16 * c, T - 1);
+      rk[SET][c] = *reinterpret_cast<const u32x4_t*>(Kb + j * row_stride + scol);
+    });
+  };
+  auto sstore = [&](int buf, auto set) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set)::value;
+    static_for<2>([&](auto c) {
+      *reinterpret_cast<u32x4_t*>(&sK[buf][(srow + 16 * c) * PITCH + scol]) = rk[SET][c];
+    });
+  };
+  auto turn = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  bf16x8_t kf[KS][NB];
+  auto read_frags = [&](int buf) __attribute__((always_inline)) {
+    static_for<KS>([&](auto s) {
+      static_for<NB>([&](auto n) {
+        kf[s][n] = *reinterpret_cast<const bf16x8_t*>(&sK[buf][(n * 32 + frow) * PITCH + s * 16 + fk]);
+      });
+    });
+  };
+  f32x16_t acc[2][NB];
+  auto any_of = [&](int kb) __attribute__((always_inline)) { return (r0 < T) && (!causal || kb * KB <= r0 + 63); };
+  auto compute = [&](int kb) __attribute__((always_inline)) {
+    if (any_of(kb)) {
+      static_for<2 * NB>([&](auto ab) { acc[ab / NB][ab % NB] = f32x16_t{}; });
+      static_for<KS>([&](auto s) {
+        static_for<2 * NB>([&](auto ab) {
+          constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
+          acc[A][N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[A][s], kf[s][N], acc[A][N], 0, 0, 0);
+        });
+      });
+    }
+  };
+  float m = -INFINITY;
+  auto reduce = [&](int kb) __attribute__((always_inline)) {
+    if (!any_of(kb)) return;
+    const int c0 = kb * KB;
+    const bool full = (!causal || c0 + KB - 1 <= r0) && (r0 + 63 < T) && (c0 + KB - 1 < T);
+    // IEEE maximum propagates NaN (v_maximum3_f32: two logits per instruction)
+    if (full) {
+      static_for<2 * NB>([&](auto ab) {
+        constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
+        static_for<8>([&](auto e) {
+          constexpr int E = 2 * decltype(e)::value;
+          m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(acc[A][N][E], acc[A][N][E + 1]));
+        });
+      });
+    } else {
+      static_for<2 * NB>([&](auto ab) {
+        constexpr int A = decltype(ab)::value / NB, N = decltype(ab)::value % NB;
+        const int j = c0 + N * 32 + (lane & 31);
+        static_for<16>([&](auto e) {
+          constexpr int E = decltype(e)::value;
+          const int i = r0 + A * 32 + 8 * (E / 4) + 4 * (lane >> 5) + (E % 4);
+          const bool ok = i < T && j < T && (!causal || j <= i);
+          m = __builtin_elementwise_maximum(m, ok ? acc[A][N][E] : -INFINITY);
+        });
+      });
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // prologue: key block 0 (both halves) and block 1's half of group 0 in LDS;
+  // group 0 holds its halves of blocks 2 and 3 in registers, group 1 its
+  // halves of blocks 1 and 2
+  gload(0, S0{});
+  sstore(0, S0{});
+  if (grp == 0) {
+    gload(1, S1{});
+    sstore(1, S1{});
+    gload(2, S0{});
+    gload(3, S1{});
+  } else {
+    gload(1, S1{});
+    gload(2, S0{});
+  }
+  turn();
+  // Turn 2k: group 0 multiplies block k while group 1 reads its fragments;
+  // turn 2k + 1: the reverse.  Block j's LDS stage (j & 1) is written by
+  // group 0 in turn 2j - 3 and by group 1 in turn 2j - 2, after the last
+  // reads of block j - 2 (turn 2j - 4) and before the first reads of block j
+  // (turn 2j - 1).
+  if (grp == 0) {
+    read_frags(0);
+    auto step = [&](int k, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;   // k & 1: register set of blocks k + 2 and k + 4
+      compute(k);
+      turn();
+      reduce(k);
+      if (k + 1 < nkb) read_frags((k + 1) & 1);
+      if (k + 2 < nkb) sstore(k & 1, std::integral_constant<int, P>{});
+      gload(k + 4, std::integral_constant<int, P>{});
+      turn();
+    };
+    int k = 0;
+    for (; k + 1 < nkb; k += 2) {
+      step(k, S0{});
+      step(k + 1, S1{});
+    }
+    if (k < nkb) step(k, S0{});
+  } else {
+    auto step = [&](int k, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;   // (k + 1) & 1: register set of blocks k + 1 and k + 3
+      if (k >= 1) reduce(k - 1);
+      read_frags(k & 1);
+      if (k + 1 < nkb) sstore((k + 1) & 1, std::integral_constant<int, P>{});
+      gload(k + 3, std::integral_constant<int, P>{});
+      turn();
+      compute(k);
+      turn();
+    };
+    int k = 0;
+    for (; k + 1 < nkb; k += 2) {
+      step(k, S1{});
+      step(k + 1, S0{});
+    }
+    if (k < nkb) step(k, S1{});
+    reduce(nkb - 1);
+  }
+
+  const int has_nan = __any(m != m) ? 1 : 0;
+  m = wave_max(m);
+  if (lane == 0) {
+    wmax[wave] = m;
+    wnan[wave] = has_nan;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float r = wmax[0];
+    int nan = wnan[0];
+    for (int w = 1; w < 8; ++w) {
+      r = fmaxf(r, wmax[w]);
+      nan |= wnan[w];
+    }
+    if (nan) r = __uint_as_float(0x7fc00000u);
+    partial[(static_cast<int64_t>(b) * H + h) * nqb + qb] = r;
+  }
+}
+
 // s_max[h] = logit_scale * max over (b, query block) of the partial maxima,
 // NaN if any partial is NaN.
 __global__ __launch_bounds__(64) void qk_reduce_kernel(const float* __restrict__ partial, int B,
@@ -306,7 +505,7 @@ hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int 
       hipLaunchKernelGGL(qk_rowmax_kernel<64>, dim3(nblocks), dim3(kThreads), 0, s, Q, K, B, T, H, causal, partial, nqb);
       break;
     case 128:
-      hipLaunchKernelGGL(qk_rowmax_kernel<128>, dim3(nblocks), dim3(kThreads), 0, s, Q, K, B, T, H, causal, partial, nqb);
+      hipLaunchKernelGGL(qk_rowmax_pp_kernel, dim3(nblocks), dim3(512), 0, s, Q, K, B, T, H, causal, partial, nqb);
       break;
     case 256:
       hipLaunchKernelGGL(qk_rowmax_kernel<256>, dim3(nblocks), dim3(kThreads), 0, s, Q, K, B, T, H, causal, partial, nqb);

@@ -497,7 +497,7 @@ def test_ns_demo_spectrum(mm, dev, rows, cols):
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("T", [1, 200, 300, 513])
+@pytest.mark.parametrize("T", [1, 200, 300, 513, 1100])
 def test_qk_rowmax_matches_oracle(mm, dev, d, causal, T):
     import torch
     say(f"[rowmax] d={d} causal={causal} T={T}")
