@@ -234,9 +234,14 @@ static void qkclip_and_friends() {
     CHECK(qkclip_rowmax_noalloc(q, q, 4, 4096, 64, 128, 0.088f, 1, s, nullptr) == MUON_OK);
     CHECK(stub_launches() == before + 2);
     CHECK(qkclip_rowmax_noalloc(q, q, 1, 256 * 4097, 64, 64, 0.125f, 1, s, nullptr) == MUON_ERR_WORKSPACE);
+    // head dim 128 runs 512-query blocks: twice the sequence fits the same scratch
+    CHECK(qkclip_rowmax_noalloc(q, q, 1, 512 * 4097, 64, 128, 0.088f, 1, s, nullptr) == MUON_ERR_WORKSPACE);
     CHECK(qkclip_rowmax_noalloc(q, q, 1, 16, 2, 96, 0.1f, 1, s, nullptr) == MUON_ERR_UNSUPPORTED);
     CHECK(qkclip_rowmax_noalloc(nullptr, q, 1, 16, 2, 64, 0.1f, 1, s, nullptr) == MUON_ERR_INVALID_ARG);
     CHECK(stub_launches() == before + 2);
+    const uint16_t* qb = static_cast<const uint16_t*>(fake(uint64_t(512) * 4096 * 64 * 128 * 2));
+    CHECK(qkclip_rowmax_noalloc(qb, qb, 1, 512 * 4096, 64, 128, 0.088f, 1, s, nullptr) == MUON_OK);
+    CHECK(stub_launches() == before + 4);
   }
   {
     const uint64_t n = uint64_t(B) * T * H * 128;

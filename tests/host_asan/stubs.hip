@@ -235,6 +235,8 @@ hipError_t launch_qk_rowmax(const bf16_t* Q, const bf16_t* K, int B, int T, int 
   need(Q, qk, "rowmax Q");
   need(K, qk, "rowmax K");
   need(partial, static_cast<uint64_t>(B) * H * nqb * 4, "rowmax partials");
+  const int q = qk_rowmax_query_block(d_head);
+  if (nqb != (T + q - 1) / q) fail("rowmax query block count");
   return hipSuccess;
 }
 
