@@ -756,7 +756,8 @@ KERNEL_NAMES = (
     ("ns_gemm_kernel<128, 128, 1>", "ns_syrk_poly [128]"), ("ns_gemm_kernel<128, 128, 2>", "ns_gemm_bx [128]"),
     ("ns_gemm_kernel<256, 128, 0>", "ns_syrk_xxt_slices"), ("ns_gemm_kernel<256, 128, 1>", "ns_syrk_poly_slices"),
     ("momentum_norm_kernel", "momentum_norm"), ("norm_finalize_kernel", "norm_finalize"),
-    ("param_update_kernel", "param_update"), ("qk_rowmax_kernel", "qk_rowmax"), ("qk_reduce_kernel", "qk_reduce"),
+    ("param_update_kernel", "param_update"), ("qk_rowmax_kernel", "qk_rowmax"), ("qk_rowmax_pp_kernel", "qk_rowmax"),
+    ("qk_reduce_kernel", "qk_reduce"),
     ("qk_rescale_kernel", "qk_rescale"), ("small_step_kernel", "small_step"), ("thin_gram_kernel", "ns_thin_gram"),
     ("thin_poly_kernel", "ns_thin_poly"), ("thin_bx_kernel", "ns_thin_bx"), ("adamw_kernel", "adamw"),
     ("attn_fwd_kernel", "attn_fwd"), ("mfma_probe_kernel", "mfma_probe"), ("dion_", "dion"))
