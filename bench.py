@@ -468,33 +468,39 @@ def copy_calibration(torch):
 
 def blas_reference(torch, reps=10):
     """hipBLASLt (torch.matmul) on the three products of one Newton-Schulz
-    iteration at the MuonClip layer's shape (4 matrices, wide 7168 x 8192),
-    computed in full (no symmetry) and without the a X / b A terms.  Operands
-    are contiguous; the result is a reference point, not part of the method."""
+    iteration, computed in full (no symmetry) and without the a X / b A terms,
+    at the MuonClip layer's shape (4 matrices, wide 7168 x 8192) and at the
+    24-layer decoder's largest shape class (72 matrices, wide 4096 x 14336).
+    Operands are contiguous; the result is a reference point, not part of the
+    method."""
     dev = torch.device("cuda:0")
-    m, n, nb = 7168, 8192, 4
-    g = torch.Generator(device=dev)
-    g.manual_seed(1)
-    Bm = (torch.randn((nb, m, m), generator=g, device=dev) * 0.01).to(torch.bfloat16)
-    X = (torch.randn((nb, m, n), generator=g, device=dev) * 0.01).to(torch.bfloat16)
-    Xt = X.transpose(1, 2).contiguous()
-    res = {"shapes": "4 x (7168x7168 @ 7168x8192, 7168x8192 @ 8192x7168, 7168x7168 @ 7168x7168)"}
-    for name, f, flop in (("B_X", lambda: torch.matmul(Bm, X), 2.0 * nb * m * m * n),
-                          ("X_Xt_full", lambda: torch.matmul(X, Xt), 2.0 * nb * m * m * n),
-                          ("A_A_full", lambda: torch.matmul(Bm, Bm), 2.0 * nb * m * m * m)):
-        f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+    out = {}
+    for key, m, n, nb in (("muonclip_layer", 7168, 8192, 4), ("decoder_4096x14336", 4096, 14336, 72)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        Bm = (torch.randn((nb, m, m), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+        X = (torch.randn((nb, m, n), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+        Xt = X.transpose(1, 2).contiguous()
+        res = {"shapes": f"{nb} x ({m}x{m} @ {m}x{n}, {m}x{n} @ {n}x{m}, {m}x{m} @ {m}x{m})"}
+        for name, f, flop in (("B_X", lambda: torch.matmul(Bm, X), 2.0 * nb * m * m * n),
+                              ("X_Xt_full", lambda: torch.matmul(X, Xt), 2.0 * nb * m * m * n),
+                              ("A_A_full", lambda: torch.matmul(Bm, Bm), 2.0 * nb * m * m * m)):
             f()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        res[name] = {"ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 1)}
-    res["ns_iteration_ms"] = round(sum(v["ms"] for k, v in res.items() if isinstance(v, dict)), 3)
-    return res
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res[name] = {"ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 1)}
+        res["ns_iteration_ms"] = round(sum(v["ms"] for k, v in res.items() if isinstance(v, dict)), 3)
+        out[key] = res
+        del Bm, X, Xt
+        torch.cuda.empty_cache()
+    return out
 
 
 def small_matrix_reading(mm, torch, dev, seed, steps=200, warmup=20):
