@@ -158,6 +158,7 @@ def main():
     # ---------------- headline: the 24-layer decoder's Muon group
     head = muon_config_run(mm, torch, dev, seed, 3, args.steps, args.warmup, roofline=True)
     note("24-layer decoder step timed")
+    out_sigma = None if args.headline_only else sigma_band(mm, torch, dev, seed)
     # the matrix-core probe runs after the headline, on a GPU already at its working clock
     peak = None if args.headline_only else mfma_peak(mm, torch, dev)
     if peak:
@@ -187,6 +188,8 @@ def main():
         out["ns_frac_measured_mfma_peak"] = round(head["ns_tflops"] / peak["tflops"], 4)
         out["roofline"]["measured_peak"] = peak["tflops"]
         out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["achieved"] / peak["tflops"], 4)
+    if out_sigma:
+        out["ns_sigma_band"] = out_sigma
     torch.cuda.empty_cache()
 
     if not args.headline_only:
@@ -331,6 +334,27 @@ def muon_config_run(mm, torch, dev, seed, idx, steps, warmup, roofline=False):
     return res
 
 
+def sigma_band(mm, torch, dev, seed, band=(0.68, 1.2)):
+    """Singular values of the Newton-Schulz output for one matrix of each of
+    the 24-layer decoder's shape classes (N(0,1) gradients, 5 quintic steps),
+    from the eigenvalues of O O^T (wide view) in fp64 on the GPU: minimum,
+    median, maximum and the share inside the band the tuned quintic leaves
+    them in ("Muon and MuonClip", Newton-Schulz interactive demo)."""
+    from synthetic import generators as gen
+    out = {}
+    for i, (r, c) in enumerate(((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336))):
+        G = gen.bulk_normal_torch((r, c), 1.0, seed + 900 + i, dev, torch.float32)
+        O = mm.ns_orthogonalize(G).double()
+        W = O if r <= c else O.t()
+        sv = torch.sqrt(torch.clamp(torch.linalg.eigvalsh(W @ W.t()), min=0.0))
+        inside = ((sv >= band[0]) & (sv <= band[1])).double().mean()
+        out[f"{r}x{c}"] = {"min": round(float(sv.min()), 4), "median": round(float(sv.median()), 4),
+                           "max": round(float(sv.max()), 4), "frac_in_band": round(float(inside), 4)}
+        del G, O, W, sv
+    torch.cuda.empty_cache()
+    return {"band": list(band), "classes": out}
+
+
 def product_roofline(prof, per_kind, steps, traffic_path):
     """The dominant Newton-Schulz product: its algorithmic flops per launch
     (flops per step over launches per step) over its average launch time."""
@@ -372,6 +396,7 @@ def muonclip_layer_reading(mm, torch, dev, seed, steps, warmup, companions=False
     """The MuonClip attention layer (hidden 7168, 64 heads x 128, batch 4 x seq
     4096): S_max on the forward's Q and K, the Muon step on W_q, W_k, W_v
     [8192x7168] and W_o [7168x8192], then the per-head W_q / W_k rescale."""
+    import numpy as np
     from synthetic import generators as gen
     wl = gen.workload(5)
     ex = wl.extra
@@ -413,6 +438,13 @@ def muonclip_layer_reading(mm, torch, dev, seed, steps, warmup, companions=False
            "ns_frac_mfma_peak": round(flop / (ns_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "ns_tflops_dense_equivalent": round(dense / (ns_ms * 1e-3) / 1e12, 1),
            "heads_clipped_per_step": int((clipped == 1).sum())}
+    # the step's telemetry (read after timing): the per-head statistic and the clip factors
+    sm = s_max.float().cpu().numpy()
+    fl = clipped.cpu().numpy()
+    clip_heads = [int(h) for h in range(H) if fl[h] == 1]
+    res["telemetry"] = {"s_max_min": round(float(sm.min()), 3), "s_max_median": round(float(np.median(sm)), 3),
+                        "s_max_max": round(float(sm.max()), 3), "tau": ex["tau"], "clipped_heads": clip_heads,
+                        "gamma_min": round(float(ex["tau"] / sm[clip_heads].max()), 5) if clip_heads else None}
     res["roofline"] = product_roofline(prof, per_kind, steps, LAYER_TRAFFIC)
     res["hbm_passes"] = hbm_passes(prof, 4 * 7168 * 8192, LAYER_TRAFFIC)
     kern = {k: {"ms_per_step": round(v[0] / steps, 4), "launches_per_step": v[1] / steps,
