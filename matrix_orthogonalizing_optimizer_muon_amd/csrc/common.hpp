@@ -97,7 +97,7 @@ enum KernelKind {
 // ---------------------------------------------------------------------------
 // Newton-Schulz GEMM launch: C[i][j] = sum_k P[i][k] * Q[j][k] over
 // `batch` matrices of a problem, every problem of a launch sharing one tile
-// size.  Epilogue: v = s * (c_acc * acc + c_e * E(i, j) + c_diag [i == j]), where s is 1,
+// size.  Epilogue: v = s * (c_acc * acc + c_e * E(i, j)), where s is 1,
 // alpha[mat] or alpha[mat]^2, and E(i, j) is read as Et[j][i] (so that a
 // lane's four consecutive rows are one 8-byte load).
 // ---------------------------------------------------------------------------
@@ -121,7 +121,6 @@ struct GemmProb {
   int mvalid, nvalid;  // outputs are written only for i < mvalid, j < nvalid
   int c16, ct16;    // 1 if C / Ct rows allow aligned 16-byte stores
   float c_acc, c_e;
-  float c_diag;     // added on the diagonal i == j (before the scale s)
 };
 
 struct GemmLaunch {

@@ -37,25 +37,22 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 // Output values of one lane for MFMA block (A, B), row group Qd: four
 // consecutive rows i0 + 32 A + 8 Qd + (0..3) of column j0 + 32 B, as fp32
-//   v = ca * acc + [i == j] cd + ce * Et[j][i]
+//   v = ca * acc + ce * Et[j][i]
 // rounded once to bf16 (v_cvt_pk_bf16_f32, nearest-even), two per dword.
 struct EpiArgs {
-  float ca, ce, cd;
+  float ca, ce;
   const bf16_t* Et;   // staged Et tile in LDS (row pitch lde), or null
   int lde;
-  int gi0, gj0;       // this lane's first row / column in the matrix (block (0, 0))
-  int li0, lj0;       // the same inside the tile
+  int li0, lj0;       // this lane's first row / column inside the tile (block (0, 0))
   int ljE;            // this lane's first row of the staged E tile (Et)
 };
 
 template <int A, int B, int Qd>
 __device__ __forceinline__ u32x2_t epi_quad(const f32x16_t& acc, const EpiArgs& e) {
-  const int i = e.gi0 + 32 * A + 8 * Qd;
-  const int j = e.gj0 + 32 * B;
   f32x4_t v;
   static_for<4>([&](auto r) {
     constexpr int R = decltype(r)::value;
-    v[R] = e.ca * acc[4 * Qd + R] + ((i + R == j) ? e.cd : 0.0f);
+    v[R] = e.ca * acc[4 * Qd + R];
   });
   if (e.Et) {
     // the Et tile staged in LDS, layout [j][i]
@@ -380,11 +377,8 @@ void ns_gemm_kernel(GemmLaunch L) {
   EpiArgs e;
   e.ca = p.c_acc * sc;
   e.ce = p.c_e * sc;
-  e.cd = p.c_diag * sc;
   e.Et = nullptr;
   e.lde = EPT;
-  e.gi0 = row0 + wr0 + 4 * (lane >> 5);
-  e.gj0 = col0 + wc0 + (lane & 31);
   e.li0 = wr0 + 4 * (lane >> 5);
   e.lj0 = wc0 + (lane & 31);
   e.ljE = e.lj0;
