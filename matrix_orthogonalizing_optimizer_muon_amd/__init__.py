@@ -333,7 +333,8 @@ def qkclip_rowmax(Q, K, logit_scale: float | None = None, causal: bool = True, o
 
 def qkclip_rowmax_noalloc(Q, K, logit_scale: float | None = None, causal: bool = True, out=None):
     """qkclip_rowmax without a workspace: the library's own per-GPU scratch
-    holds the partial maxima (B * H * ceil(T / 256) of them, at most
+    holds the partial maxima (B * H * ceil(T / q) of them, q = 512 queries
+    per block for d_head 128 and 256 otherwise, at most
     qkclip_rowmax_noalloc_max_partials()).  Calls that overlap on one GPU
     race.  Returns fp32 [H]."""
     torch = _torch()

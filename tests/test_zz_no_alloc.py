@@ -66,7 +66,8 @@ def test_noalloc_rowmax_matches_workspace_entry(mm, causal):
 
 
 def test_noalloc_rowmax_refuses_beyond_its_scratch(mm):
-    """B * H * ceil(T / 256) one past the scratch: MUON_ERR_WORKSPACE, decided
+    """B * H * ceil(T / 256) one past the scratch (head dim 64 runs 256-query
+    blocks): MUON_ERR_WORKSPACE, decided
     on the host before any launch (the tensors are never read)."""
     import torch
     lib = mm.load_library()
