@@ -44,12 +44,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][kKB * kKP];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][kD * kVP];
 
-  // each XCD walks a contiguous range of (head, query block) pairs, one head's
-  // query blocks back to back (longest causal rows first), so a head's K and V
-  // are fetched into that XCD's L2 once
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / A.nqb;
-  const int qb = A.nqb - 1 - (lin - bh * A.nqb);
+  // Each XCD (block b runs on XCD b % 8) owns a contiguous range of heads and
+  // walks it in groups of 4 heads, the group's query blocks heaviest first
+  // (longest causal rows first across the group): the heads of a group share
+  // that XCD's L2 for their K and V, and the short blocks fill the end of each
+  // group.  Head counts that do not split that way fall back to one head's
+  // query blocks at a time.
+  int bh, qb;
+  if (!xcd_group_order(blockIdx.x, A.B * A.H, A.nqb, 4, &bh, &qb)) {
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    bh = lin / A.nqb;
+    qb = A.nqb - 1 - (lin - bh * A.nqb);
+  }
   const int b = bh / A.H, head = bh - b * A.H;
   const int T = A.T;
   const int64_t tok = static_cast<int64_t>(A.H) * kD;                 // token stride

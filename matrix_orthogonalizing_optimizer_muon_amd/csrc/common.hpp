@@ -65,6 +65,22 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
 }
 
+// Block order for causal grids of (head, query block) pairs, heaviest first
+// inside small groups of heads: block b runs on XCD b % 8; when nbh heads
+// split into 8 ranges of whole groups of gh, XCD x walks its range group by
+// group, each group's query blocks heaviest first across its heads (qb
+// counts down).  The heads of a group share the XCD's L2, and the light
+// blocks of a group fill in behind its heavy ones.  Returns false (and sets
+// nothing) when nbh does not split that way.
+__device__ __forceinline__ bool xcd_group_order(int b, int nbh, int nqb, int gh, int* bh, int* qb) {
+  if (nbh % (8 * gh) != 0) return false;
+  const int x = b % 8, idx = b / 8;
+  const int g = idx / (gh * nqb), r = idx - g * (gh * nqb);
+  *qb = nqb - 1 - r / gh;
+  *bh = x * (nbh / 8) + g * gh + r % gh;
+  return true;
+}
+
 // Kernel kinds, used by the optional event profiler.
 enum KernelKind {
   KIND_MOMENTUM_NORM = 0,

@@ -15,9 +15,12 @@
 // Maxima are reduced across the wavefront with cross-lane max, across the
 // block through LDS, and across blocks by a second, fixed-order kernel (no
 // atomics, no initialisation pass).  Blocks are numbered heaviest query block
-// first across all (batch row, head) pairs: the dispatcher hands them out in
-// that order, so the long causal rows start first on every CU and the short
-// ones fill the end.
+// first: each XCD (block b runs on XCD b % 8) owns a contiguous range of
+// (batch row, head) pairs and walks it in groups of 8, the group's query
+// blocks heaviest first, so the long causal rows start first on every CU, the
+// short ones fill the end, and the group's heads share the XCD's L2 for K.
+// Head counts that do not split that way take the same order across all
+// pairs.
 #include <algorithm>
 #include <mutex>
 
@@ -87,8 +90,11 @@ void qk_rowmax_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
   __shared__ int wnan[kWaves];
 
   const int nbh = B * H;
-  const int bh = blockIdx.x % nbh;
-  const int qb = nqb - 1 - blockIdx.x / nbh;  // heaviest query blocks first
+  int bh, qb;
+  if (!xcd_group_order(blockIdx.x, nbh, nqb, 8, &bh, &qb)) {
+    bh = blockIdx.x % nbh;                 // heaviest query blocks of every pair first
+    qb = nqb - 1 - blockIdx.x / nbh;
+  }
   const int b = bh / H, h = bh - b * H;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -248,8 +254,11 @@ void qk_rowmax_pp_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict_
   __shared__ int wnan[8];
 
   const int nbh = B * H;
-  const int bh = blockIdx.x % nbh;
-  const int qb = nqb - 1 - blockIdx.x / nbh;  // heaviest query blocks first
+  int bh, qb;
+  if (!xcd_group_order(blockIdx.x, nbh, nqb, 8, &bh, &qb)) {
+    bh = blockIdx.x % nbh;                 // heaviest query blocks of every pair first
+    qb = nqb - 1 - blockIdx.x / nbh;
+  }
   const int b = bh / H, h = bh - b * H;
 
   const int tid = threadIdx.x, lane = tid & 63;
