@@ -92,7 +92,12 @@ typedef struct {
 
 /* One group of same-shape matrices.  param/grad: param dtype; momentum: fp32;
  * all three [batch][rows][cols] with the same batch_stride (in elements,
- * >= rows*cols).  param and momentum are updated in place; grad is read. */
+ * >= rows*cols).  param and momentum are updated in place; grad is read.
+ * Size limit, here and in ns_orthogonalize: rows, cols <= 2^20 and
+ * (max(rows, cols) + 256) * (min(rows, cols) + 256) <= 2^31, about 2.1e9
+ * elements per matrix (8192 x 253944, 46084 x 46084); beyond it the calls
+ * return MUON_ERR_INVALID_ARG and the workspace queries 0.  batch and
+ * batch_stride are not limited. */
 typedef struct {
   void* param;
   const void* grad;

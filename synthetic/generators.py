@@ -98,6 +98,27 @@ def log_spaced_levels(k: int, levels: int = 16, cond: float = 1000.0) -> np.ndar
     return np.repeat(lv, reps)
 
 
+def partial_permutation(g: np.random.Generator, rows: int, cols: int, sigma):
+    """A rows x cols matrix with one nonzero per row of its wide view
+    (min(rows, cols) nonzeros, no two in one row or column): the nonzero of
+    wide-view row i sits at a seeded distinct position along the long side,
+    which always includes the last one, and holds sigma[i] with a seeded sign.
+    Returned as (row index, column index, value) arrays in the matrix's own
+    layout, so that a full-size matrix never has to exist on the host.  Its
+    singular values are |sigma| and its singular vectors coordinate vectors."""
+    k, n = min(rows, cols), max(rows, cols)
+    sigma = np.asarray(sigma, dtype=np.float64)
+    assert sigma.shape == (k,)
+    long_idx = g.choice(n, size=k, replace=False)
+    if not np.any(long_idx == n - 1):
+        long_idx[g.integers(k)] = n - 1
+    vals = sigma[g.permutation(k)] * np.where(g.random(k) < 0.5, -1.0, 1.0)
+    short_idx = np.arange(k)
+    if rows <= cols:
+        return short_idx, long_idx.astype(np.int64), vals
+    return long_idx.astype(np.int64), short_idx, vals
+
+
 def zipf_magnitudes(g: np.random.Generator, n: int, s: float = 1.1) -> np.ndarray:
     """Per-expert magnitude rank^-s over a seeded permutation of ranks 1..n
     (the largest is 1)."""

@@ -106,6 +106,29 @@ def test_host_validation_without_gpu(lib):
     assert lib.ns_workspace_size(1, 0, 4) == 0
 
 
+def test_size_limits_without_gpu(lib):
+    """The largest matrices accepted: every side <= 2^20 and the padded wide
+    view (max + 256) x (min + 256) <= 2^31 elements; one more row or column
+    is refused before any launch."""
+    import matrix_orthogonalizing_optimizer_muon_amd as mm
+    accepted = [(8192, 253944), (253944, 8192), (46084, 46084), (1 << 20, 1), (1, 1 << 20)]
+    refused = [(8192, 253945), (253945, 8192), (46085, 46085), ((1 << 20) + 1, 1), (1, (1 << 20) + 1)]
+    for r, c in accepted:
+        assert lib.ns_workspace_size(1, r, c) > 0, (r, c)
+    for r, c in refused:
+        assert lib.ns_workspace_size(1, r, c) == 0, (r, c)
+        assert lib.ns_orthogonalize(16, mm.DTYPE_BF16, 16, 1, r, c, r * c, 5, 3.4445, -4.775, 2.0315,
+                                    1e-7, 256, 1 << 40, None) == mm.MUON_ERR_INVALID_ARG
+        g = (mm._Group * 1)()
+        g[0] = mm._Group(16, 16, 16, 1, r, c, 0, r * c)
+        assert lib.muon_step_workspace_size(g, 1) == 0
+        hp = mm.HParams().to_c()
+        assert lib.muon_step(g, 1, mm.DTYPE_BF16, ctypes.byref(hp), 256, 1 << 40, None) == mm.MUON_ERR_INVALID_ARG
+    # the workspace of the largest square case: four padded copies of X and
+    # two of A (46336 x 46336 bf16 each) plus the norm partials
+    assert lib.ns_workspace_size(1, 46084, 46084) >= 6 * 46336 * 46336 * 2
+
+
 def test_workspace_layout_query(lib):
     import matrix_orthogonalizing_optimizer_muon_amd as mm
     g = (mm._Group * 2)()

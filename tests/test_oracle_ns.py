@@ -14,6 +14,10 @@ What each test pins, and against what:
     Express aside (tests/golden/polar_express_aside.json).
   * band: outputs stay in [0.68, 1.2025] for inputs >= 0.0015 (demo text).
   * orientation: the transposed input gives the transposed output.
+  * decoupling: on a scaled partial permutation (coordinate singular vectors)
+    the full iteration equals the per-element scalar map and keeps every
+    other element zero, which the full-size GPU checks at the element limit
+    rely on.
 """
 import json
 import os
@@ -147,3 +151,27 @@ def test_scale_invariance():
     a = O.newton_schulz(G, eps=0.0)
     b = O.newton_schulz(G * 1234.5, eps=0.0)
     assert np.allclose(a, b, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape", [(24, 60), (60, 24), (16, 16)])
+def test_partial_permutation_decouples(shape):
+    """One nonzero per row of the wide view, at distinct columns: the matrix
+    is U diag(s) V^T with coordinate vectors U, V, so the iteration keeps the
+    pattern and maps each nonzero through the scalar polynomial alone.  The
+    full-size GPU checks rest on this: the oracle's iteration on the 1 x 1
+    matrix [[x / ||G||_F]] must equal the oracle's full-matrix result at that
+    element, and every other element must stay exactly zero."""
+    from synthetic import generators as gen
+    rows, cols = shape
+    g = gen.rng(rows * 1000 + cols)
+    ri, ci, v = gen.partial_permutation(g, rows, cols, gen.log_spaced_levels(min(rows, cols), 4))
+    G = np.zeros(shape)
+    G[ri, ci] = v
+    assert np.count_nonzero(G) == min(rows, cols)
+    assert np.linalg.matrix_rank(G) == min(rows, cols)
+    full = O.newton_schulz(G)
+    x = O.frobenius_normalize(v[None, :], 1e-7)[0]
+    per = np.array([O.newton_schulz_iterate(np.array([[t]]), 5, *TUNED)[0, 0] for t in x])
+    assert np.array_equal(full != 0, G != 0)
+    assert np.allclose(full[ri, ci], per, rtol=1e-13, atol=0)
+    assert np.allclose(per, scalar_composed(x, 5, TUNED), rtol=1e-13, atol=0)
