@@ -21,6 +21,7 @@ stated 2e-2 relative Frobenius error.  The Muon step also checks the momentum
 (every element), 1 / ||U||_F and the parameter update at the nonzeros and at
 a seeded sample of other positions, where the update is the pure decay.
 """
+import math
 import sys
 
 import numpy as np
@@ -149,3 +150,86 @@ def test_muon_step_at_the_element_limit(mm):
     assert einv <= 1e-5
     assert eo <= 2e-2
     assert ew == 0
+
+
+# ---------------------------------------------------------------------------
+# S_max past 2^31 elements of Q and K
+# ---------------------------------------------------------------------------
+
+def plant(Q, K, h, i, j, vq, vk):
+    import torch
+    Q[0, i, h] = torch.from_numpy(vq).to(Q.device, Q.dtype)
+    K[0, j, h] = torch.from_numpy(vk).to(K.device, K.dtype)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_qk_rowmax_long_context(mm, d):
+    """One batch row of 131072 tokens and 16384 / d heads: Q and K hold 2^31
+    elements each, so byte offsets reach 2^32.  Q and K are N(0, 1/256) apart
+    from two planted pairs per head: an allowed pair (j <= i) whose logit is
+    d, and a masked pair (j > i) whose logit is 2.25 d.  Cauchy-Schwarz on the
+    measured row norms bounds every other logit below d, so the causal
+    statistic is exactly d * logit_scale and the unmasked one 2.25 d *
+    logit_scale (integer sums of products of +-1 and +-1.5, exact in fp32).
+    Head 0 places its allowed pair at the farthest distance (i = T - 1,
+    j = 0) and head 1 on the last diagonal element.  At d = 128 the
+    attention forward's S_max export is held to the same value."""
+    import torch
+    dev = torch.device("cuda:0")
+    B, T, H = 1, 131072, 16384 // d
+    say(f"[qk long context] B={B} T={T} H={H} d={d}")
+    Q = gen.bulk_normal_torch((B, T, H, d), 1.0 / 16, 81 + d, dev, torch.bfloat16)
+    K = gen.bulk_normal_torch((B, T, H, d), 1.0 / 16, 82 + d, dev, torch.bfloat16)
+    g = gen.rng(83 + d)
+    planted = []
+    for h in range(H):
+        if h == 0:
+            i, j = T - 1, 0
+        elif h == 1:
+            i, j = T - 1, T - 1
+        else:
+            i = int(g.integers(0, T))
+            j = int(g.integers(0, i + 1))
+        # the masked pair takes other rows of Q and K than the allowed one
+        i2, j2 = i, j
+        while i2 == i or j2 == j:
+            i2 = int(g.integers(0, T - 1))
+            j2 = int(g.integers(i2 + 1, T))
+        v = np.where(g.random(d) < 0.5, -1.0, 1.0)
+        w = 1.5 * np.where(g.random(d) < 0.5, -1.0, 1.0)
+        plant(Q, K, h, i, j, v, v)
+        plant(Q, K, h, i2, j2, w, w)
+        planted.append((i, j, i2, j2, v, w))
+    # Cauchy-Schwarz bound on every pair other than the two planted ones
+    qn = Q.float().norm(dim=3)   # [B, T, H]
+    kn = K.float().norm(dim=3)
+    for h, (i, j, i2, j2, v, w) in enumerate(planted):
+        qn[0, i, h] = 0.0
+        qn[0, i2, h] = 0.0
+        kn[0, j, h] = 0.0
+        kn[0, j2, h] = 0.0
+    bq, bk = float(qn.max()), float(kn.max())
+    del qn, kn
+    big = 1.5 * math.sqrt(d)
+    for i, j, i2, j2, v, w in planted:
+        cross = [abs(float(v @ w))] * 2     # q_i . k_j2 and q_i2 . k_j
+        bound = max(bq * bk, big * bq, big * bk, *cross)
+        assert bound < 0.9 * d, (bound, d)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    want_c = np.float32(np.float32(scale) * np.float32(d))
+    want_n = np.float32(np.float32(scale) * np.float32(2.25 * d))
+    got_c = to_host(mm.qkclip_rowmax(Q, K, scale, True))
+    got_n = to_host(mm.qkclip_rowmax(Q, K, scale, False))
+    torch.cuda.synchronize()
+    say(f"   causal {got_c.min():.6g}..{got_c.max():.6g} (want {want_c:.6g}); "
+        f"unmasked {got_n.min():.6g}..{got_n.max():.6g} (want {want_n:.6g})")
+    assert np.all(got_c == want_c)
+    assert np.all(got_n == want_n)
+    if d == 128:
+        # the attention forward's S_max export reads the same logits (K as V)
+        _, sm, _ = mm.attn_fwd(Q, K, K, scale, True)
+        got_a = to_host(sm)
+        torch.cuda.synchronize()
+        say(f"   attention causal {got_a.min():.6g}..{got_a.max():.6g}")
+        assert np.all(got_a == want_c)
