@@ -740,12 +740,12 @@ def blas_info():
     return threads, vendor
 
 
-def cpu_baseline_decoder(seed, iters=1):
+def cpu_baseline_decoder(seed, iters=2):
     """Time the fp64 oracle on a bounded sample of the headline workload and
-    extrapolate to one step: per shape class of the 24-layer decoder, one
-    Newton-Schulz iteration and the momentum / lookahead / normalisation /
-    update pass of one matrix; a step is each class's matrix count times
-    (5 iterations + that pass).  Inputs are N(0, 1) draws of the class's
+    extrapolate to one step: per shape class of the 24-layer decoder, `iters`
+    Newton-Schulz iterations (timed together, averaged) and the momentum /
+    lookahead / normalisation / update pass of one matrix; a step is each
+    class's matrix count times (5 iterations + that pass).  Inputs are N(0, 1) draws of the class's
     shape (the oracle's time does not depend on the values)."""
     import numpy as np
 
@@ -774,7 +774,7 @@ def cpu_baseline_decoder(seed, iters=1):
                        O.update_scale(gr.rows, gr.cols))
         t_elem += time.perf_counter() - t0
         step_s += gr.batch * (wl.ns_steps * t_iter + t_elem)
-        parts.append(f"{gr.rows}x{gr.cols}: {t_iter:.2f} s per iteration + {t_elem:.2f} s")
+        parts.append(f"{gr.rows}x{gr.cols}: {t_iter:.2f} s per iteration (mean of {iters}) + {t_elem:.2f} s")
     sample_s = time.perf_counter() - t_all
     return {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": threads, "kind": "oracle",
             "blas": vendor,
