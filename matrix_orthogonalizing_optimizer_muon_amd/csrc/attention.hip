@@ -17,6 +17,11 @@
 //   O^T += V^T P^T (d x queries: the softmax rescale is a per-lane scalar)
 // P takes the keys in the order its accumulator registers hold them; V^T is
 // read in the same order, which leaves the contraction unchanged.
+// The probabilities are exp2(s c2 - r) against a reference r that moves only
+// when a query's running maximum passes it by more than 8 (in log2 units):
+// the ratio O = sum p v / sum p does not depend on r, p stays below 2^8, and
+// the rescale of O and of the running sum is skipped for most key blocks.
+// The exact running maximum is still kept for the statistic.
 #include <cmath>
 
 #include "common.hpp"
@@ -120,6 +125,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   f32x16_t o[kD / 32];
   static_for<kD / 32>([&](auto i) { o[i] = f32x16_t{}; });
   float m_run = -INFINITY, l_run = 0.0f;
+  float mref = -INFINITY;   // exponent reference: m_run * c2 <= mref + 8
   int nanf = 0;
   const float c2 = A.c2;
 
@@ -151,15 +157,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     });
     nanf |= (mloc != mloc);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    float alpha = 1.0f, mc = 0.0f;
-    if (m_new != -INFINITY) {
-      alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      mc = m_new * c2;
+    m_run = fmaxf(m_run, mloc);
+    // move the exponent reference (and rescale) only where the maximum has
+    // passed it by more than 8; one wave-wide test per key block
+    const float mn2 = m_run * c2;
+    const bool up = mn2 > mref + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float nref = up ? mn2 : mref;
+      const float alpha = (mref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mref - nref);
+      mref = nref;
+      l_run *= alpha;
+      static_for<kD / 32>([&](auto i) { o[decltype(i)::value] = o[decltype(i)::value] * alpha; });
     }
-    m_run = m_new;
-    l_run *= alpha;
-    static_for<kD / 32>([&](auto i) { o[decltype(i)::value] = o[decltype(i)::value] * alpha; });
+    const float mc = (mref == -INFINITY) ? 0.0f : mref;
     bf16x8_t pb[4];
     static_for<32>([&](auto i) {
       constexpr int MB = decltype(i)::value / 16, E = decltype(i)::value % 16;
@@ -221,7 +231,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
       });
     });
     if (A.lse && hf == 0)
-      A.lse[(static_cast<int64_t>(b) * A.H + head) * T + q] = m_run * A.scale + logf(l_tot);
+      A.lse[(static_cast<int64_t>(b) * A.H + head) * T + q] =
+          (mref == -INFINITY ? 0.0f : mref * 0.69314718055994531f) + logf(l_tot);   // r ln 2 = (r / c2) scale
   }
   const float mw = wave_max64(q < T ? m_run : -INFINITY);
   const int anynan = __any(q < T && nanf);
