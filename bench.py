@@ -191,10 +191,18 @@ def main():
     if out_sigma:
         out["ns_sigma_band"] = out_sigma
     torch.cuda.empty_cache()
+    hbm = None if args.headline_only else hbm_ceiling(mm, torch, dev)
+    if hbm:
+        out["hbm_measured_ceiling"] = hbm
+        attach_hbm_ceiling(out["hbm_passes"], hbm)
+        note(f"HBM stream probe: {hbm['mix_6r_8w_GBs']} GB/s for the momentum pass's mix, "
+             f"{hbm['mix_4r_2w_GBs']} for the update's, {hbm['copy_GBs']} for a copy")
 
     if not args.headline_only:
         out["muonclip_layer"] = muonclip_layer_reading(mm, torch, dev, seed, args.steps, args.warmup,
                                                        companions=True)
+        if hbm:
+            attach_hbm_ceiling(out["muonclip_layer"]["hbm_passes"], hbm)
         note("MuonClip layer step timed")
         out["layer_hidden2048"] = muon_config_run(mm, torch, dev, seed, 2, args.steps, args.warmup)
         note("hidden-2048 layer timed")
@@ -244,6 +252,46 @@ def mfma_peak(mm, torch, dev, iters=8000):
             "smooth_operands_tflops": round(best[mm.PROBE_SMOOTH], 1),
             "probe": f"{blocks} blocks x 4 waves x 32 x {iters} v_mfma_f32_32x32x16_bf16 on random bf16 "
                      "register operands (smooth operands beside it), best of 3 after ~80 ms of warm-up"}
+
+
+def hbm_ceiling(mm, torch, dev, gib=3):
+    """The HBM stream probe (muon_hbm_probe) on `gib` GiB streams for the
+    read/write mixes of the two passes and a plain copy: 6 B read and 8 B
+    written per element (the momentum pass with its transposed X0 copy),
+    4 B read and 2 B written (the update pass), 1:1.  Best of 3 timed
+    launches after 3 warm-up launches per mix and launch shape (1 or 4 units
+    per thread), HIP events on the current stream."""
+    n = gib << 30
+    src = torch.empty(n // 4, dtype=torch.int32, device=dev)
+    src.random_()
+    dst = torch.empty(n // 4, dtype=torch.int32, device=dev)
+    res = {}
+    for key, r, w in (("mix_6r_8w_GBs", 3, 4), ("mix_4r_2w_GBs", 2, 1), ("copy_GBs", 1, 1)):
+        best = 0.0
+        for unroll in (1, 4):
+            for _ in range(3):
+                mm.hbm_probe(src, dst, r, w, unroll)
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                moved = mm.hbm_probe(src, dst, r, w, unroll)
+                e1.record()
+                torch.cuda.synchronize()
+                best = max(best, moved / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        res[key] = round(best, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    res["probe"] = (f"nontemporal 16-byte loads and stores, 1 KB per wave instruction, {gib} GiB streams, "
+                    "1 or 4 units per thread, best of 3 after 3 warm-up launches per mix and shape")
+    return res
+
+
+def attach_hbm_ceiling(passes, hbm):
+    """Each HBM pass's moved bytes against the probe's rate for its mix."""
+    for k, key in (("momentum_norm", "mix_6r_8w_GBs"), ("param_update", "mix_4r_2w_GBs")):
+        if k in passes and hbm.get(key):
+            passes[k]["frac_of_measured_ceiling"] = round(passes[k]["GBs_moved"] / hbm[key], 4)
 
 
 def make_config_groups(mm, torch, dev, seed, idx):

@@ -343,6 +343,22 @@ const char* muon_status_string(int status);
 #define MUON_PROBE_SMOOTH 1
 int muon_mfma_probe(int blocks, int iters, int operands, float* sink, hipStream_t stream);
 
+/* HBM stream probe (not part of the optimizer): units = min(src_bytes /
+ * (16 reads), dst_bytes / (16 writes)); unit u reads the 16-byte chunks
+ * src[i * units + u], i < reads, and writes dst[k * units + u], k < writes
+ * (the XOR of its loads with k in the first word), all nontemporal, so every
+ * wave instruction moves 1 KB of consecutive bytes; each thread takes
+ * `unroll` units (1 or 4), all their loads issued first.  Timed with events on
+ * `stream`, it gives the HBM rate this chip sustains for a read/write mix:
+ * (reads, writes) = (3, 4) is the momentum pass's 6 B read and 8 B written
+ * per element, (2, 1) the update pass's, (1, 1) a copy.  src and dst: device,
+ * 16-byte aligned, not overlapping.  Returns the bytes the launch moves
+ * (units * 16 * (reads + writes)), or minus an error code: an unlisted mix,
+ * null or misaligned pointers, another unroll, or units outside 1..2^36 give
+ * -MUON_ERR_INVALID_ARG, a failed launch -MUON_ERR_HIP. */
+int64_t muon_hbm_probe(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int reads,
+                       int writes, int unroll, hipStream_t stream);
+
 /* Optional per-kernel timing with HIP events recorded around every launch
  * the library makes on the caller's stream.  muon_profile_enable(1) clears
  * and starts recording; muon_profile_collect() waits for the recorded events,

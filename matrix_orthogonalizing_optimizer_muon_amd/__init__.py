@@ -121,6 +121,8 @@ def load_library() -> ctypes.CDLL:
     lib.adamw_step.restype = i32
     lib.muon_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
     lib.muon_mfma_probe.restype = i32
+    lib.muon_hbm_probe.argtypes = [vp, sz, vp, sz, i32, i32, i32, vp]
+    lib.muon_hbm_probe.restype = i64
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_profile_enable.argtypes = [i32]
@@ -550,6 +552,20 @@ def mfma_probe(blocks: int, iters: int, sink, operands: int = PROBE_RANDOM):
     _check(load_library().muon_mfma_probe(blocks, iters, int(operands), sink.data_ptr(), _stream()),
            "muon_mfma_probe")
     return blocks * 4 * 32 * iters * 32768
+
+
+def hbm_probe(src, dst, reads: int, writes: int, unroll: int = 1):
+    """Launch the HBM stream probe on the current stream (see muon_hbm_probe):
+    src and dst are device tensors (their bytes are the streams), (reads,
+    writes) one of (1, 1), (3, 4), (2, 1), unroll 1 or 4 units per thread.
+    Returns the bytes the launch moves."""
+    _need_cuda(src, dst)
+    moved = load_library().muon_hbm_probe(src.data_ptr(), src.numel() * src.element_size(), dst.data_ptr(),
+                                          dst.numel() * dst.element_size(), int(reads), int(writes), int(unroll),
+                                          _stream())
+    if moved < 0:
+        _check(int(-moved), "muon_hbm_probe")
+    return int(moved)
 
 
 def profile_enable(on: bool = True):

@@ -983,6 +983,18 @@ int muon_mfma_probe(int blocks, int iters, int operands, float* sink, hipStream_
   return MUON_OK;
 }
 
+int64_t muon_hbm_probe(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int reads, int writes,
+                       int unroll, hipStream_t stream) {
+  const bool mix = (reads == 1 && writes == 1) || (reads == 3 && writes == 4) || (reads == 2 && writes == 1);
+  if (!src || !dst || !mix || !aligned(src, 16) || !aligned(dst, 16)) return -MUON_ERR_INVALID_ARG;
+  if (unroll != 1 && unroll != 4) return -MUON_ERR_INVALID_ARG;
+  const int64_t units = static_cast<int64_t>(std::min(src_bytes / (16 * static_cast<size_t>(reads)),
+                                                      dst_bytes / (16 * static_cast<size_t>(writes))));
+  if (units < 1 || units > (int64_t(1) << 36)) return -MUON_ERR_INVALID_ARG;
+  if (launch_hbm_probe(src, dst, units, reads, writes, unroll, stream) != hipSuccess) return -MUON_ERR_HIP;
+  return units * 16 * (reads + writes);
+}
+
 int muon_profile_enable(int on) {
   for (auto& r : g_prof) {
     g_event_pool.push_back(r.a);

@@ -384,6 +384,8 @@ hipError_t launch_adamw(const AdamWLaunch& A, int dtype, int blocks, hipStream_t
 // Register-only bf16 MFMA loop (probe.hip): 256-thread blocks, each wave
 // issuing 4 x iters v_mfma_f32_32x32x16_bf16.
 hipError_t launch_mfma_probe(int blocks, int iters, int operands, float* sink, hipStream_t s);
+hipError_t launch_hbm_probe(const void* src, void* dst, int64_t units, int reads, int writes, int unroll,
+                            hipStream_t s);
 
 // Profiler hooks (api.hip).
 void prof_begin(int kind, hipStream_t s);

@@ -1,5 +1,5 @@
 // Matrix-core rate probe: bf16 MFMAs on register operands only, no memory
-// traffic in the loop.  It measures the rate the chip sustains on its matrix
+// traffic in the loop (and, at the end of the file, an HBM stream probe).  It measures the rate the chip sustains on its matrix
 // cores at the clock it holds under that load, the reference point beside the
 // 2.5 PFLOP/s dense bf16 figure of the specification.  Not part of the
 // optimizer step.
@@ -63,7 +63,62 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* sink)
   if (tid == 0) sink[blockIdx.x] = s;
 }
 
+// HBM stream probe: unit u of a launch reads R 16-byte chunks of src and
+// writes W 16-byte chunks of dst, chunk i of every unit side by side
+// (src[i * units + u]), so each load and store instruction of a wave covers
+// 1 KB of consecutive bytes.  A thread takes U units 256 apart and issues
+// all of their loads before any store (R * U loads in flight).  Loads and
+// stores are nontemporal, as in the optimizer's passes.  Stored chunk k is
+// the XOR of the unit's loads with k in its first word, so no load can be
+// dropped.
+template <int R, int W, int U>
+__global__ __launch_bounds__(256) void hbm_probe_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                        int64_t units) {
+  const int64_t u0 = static_cast<int64_t>(blockIdx.x) * (256 * U) + threadIdx.x;
+  u32x4_t v[U][R];
+  static_for<U>([&](auto j) {
+    const int64_t u = min(u0 + 256 * decltype(j)::value, units - 1);   // the tail reloads the last unit
+    static_for<R>([&](auto i) {
+      v[decltype(j)::value][decltype(i)::value] = __builtin_nontemporal_load(src + decltype(i)::value * units + u);
+    });
+  });
+  static_for<U>([&](auto j) {
+    constexpr int J = decltype(j)::value;
+    const int64_t u = u0 + 256 * J;
+    if (u >= units) return;
+    u32x4_t x = v[J][0];
+    static_for<R - 1>([&](auto i) { x ^= v[J][decltype(i)::value + 1]; });
+    static_for<W>([&](auto k) {
+      u32x4_t y = x;
+      y[0] ^= static_cast<uint32_t>(decltype(k)::value);
+      __builtin_nontemporal_store(y, dst + decltype(k)::value * units + u);
+    });
+  });
+}
+
 }  // namespace
+
+template <int R, int W>
+hipError_t launch_hbm_mix(const u32x4_t* in, u32x4_t* out, int64_t units, int unroll, hipStream_t s) {
+  const dim3 block(256);
+  if (unroll == 1)
+    hipLaunchKernelGGL((hbm_probe_kernel<R, W, 1>), dim3(static_cast<unsigned>((units + 255) / 256)), block, 0, s,
+                       in, out, units);
+  else
+    hipLaunchKernelGGL((hbm_probe_kernel<R, W, 4>), dim3(static_cast<unsigned>((units + 1023) / 1024)), block, 0, s,
+                       in, out, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_hbm_probe(const void* src, void* dst, int64_t units, int reads, int writes, int unroll,
+                            hipStream_t s) {
+  const u32x4_t* in = static_cast<const u32x4_t*>(src);
+  u32x4_t* out = static_cast<u32x4_t*>(dst);
+  if (reads == 1 && writes == 1) return launch_hbm_mix<1, 1>(in, out, units, unroll, s);
+  if (reads == 3 && writes == 4) return launch_hbm_mix<3, 4>(in, out, units, unroll, s);
+  if (reads == 2 && writes == 1) return launch_hbm_mix<2, 1>(in, out, units, unroll, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_mfma_probe(int blocks, int iters, int operands, float* sink, hipStream_t s) {
   if (operands == MUON_PROBE_RANDOM)

@@ -210,6 +210,15 @@ static void invalid_arguments() {
   CHECK(muon_mfma_probe(1, 1, MUON_PROBE_RANDOM, nullptr, nullptr) == MUON_ERR_INVALID_ARG);
   CHECK(muon_mfma_probe(1, 1, 2, s, nullptr) == MUON_ERR_INVALID_ARG);
   CHECK(muon_mfma_probe(1, (1 << 24) + 1, MUON_PROBE_SMOOTH, s, nullptr) == MUON_ERR_INVALID_ARG);
+  {
+    void* a = fake(4096);
+    void* b = fake(4096);
+    CHECK(muon_hbm_probe(a, 4096, b, 4096, 2, 2, 1, nullptr) == -MUON_ERR_INVALID_ARG);
+    CHECK(muon_hbm_probe(a, 4096, b, 4096, 1, 1, 2, nullptr) == -MUON_ERR_INVALID_ARG);
+    CHECK(muon_hbm_probe(nullptr, 4096, b, 4096, 1, 1, 1, nullptr) == -MUON_ERR_INVALID_ARG);
+    CHECK(muon_hbm_probe(a, 4096, b, 8, 3, 4, 4, nullptr) == -MUON_ERR_INVALID_ARG);   // no whole unit
+    CHECK(muon_hbm_probe(static_cast<char*>(a) + 8, 4000, b, 4096, 1, 1, 1, nullptr) == -MUON_ERR_INVALID_ARG);
+  }
   for (int k = 0; k < 5; ++k) CHECK(muon_status_string(k) && strlen(muon_status_string(k)) > 0);
   CHECK(stub_launches() == 0);
 }
@@ -296,6 +305,12 @@ static void qkclip_and_friends() {
     float* sink = static_cast<float*>(fake(512 * 4));
     CHECK(muon_mfma_probe(512, 10, MUON_PROBE_RANDOM, sink, nullptr) == MUON_OK);
     CHECK(muon_mfma_probe(512, 10, MUON_PROBE_SMOOTH, sink, nullptr) == MUON_OK);
+    // the HBM probe: units from the smaller stream, every chunk inside both
+    void* src = fake(3 * 16 * 1000 + 40);
+    void* dst = fake(4 * 16 * 1001);
+    CHECK(muon_hbm_probe(src, 3 * 16 * 1000 + 40, dst, 4 * 16 * 1001, 3, 4, 4, nullptr) == 1000 * 16 * 7);
+    CHECK(muon_hbm_probe(src, 32 * 1000, dst, 16 * 999, 2, 1, 1, nullptr) == 999 * 16 * 3);
+    CHECK(muon_hbm_probe(src, 16 * 7, dst, 16 * 7, 1, 1, 4, nullptr) == 7 * 16 * 2);
   }
   // the profiler: on, one call, collect, off
   CHECK(muon_profile_enable(1) == MUON_OK);

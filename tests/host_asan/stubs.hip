@@ -348,4 +348,14 @@ hipError_t launch_mfma_probe(int blocks, int iters, int operands, float* sink, h
   return hipSuccess;
 }
 
+hipError_t launch_hbm_probe(const void* src, void* dst, int64_t units, int reads, int writes, int unroll,
+                            hipStream_t) {
+  ++g_launches;
+  const bool mix = (reads == 1 && writes == 1) || (reads == 3 && writes == 4) || (reads == 2 && writes == 1);
+  if (units < 1 || !mix || (unroll != 1 && unroll != 4)) fail("hbm probe args");
+  need(src, static_cast<uint64_t>(units) * 16 * reads, "hbm probe src");
+  need(dst, static_cast<uint64_t>(units) * 16 * writes, "hbm probe dst");
+  return hipSuccess;
+}
+
 }  // namespace muon
