@@ -132,8 +132,9 @@ def main():
         summarize_clock(args.summarize_clock)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(the step shards by whole matrices across GPUs, which is not built here)",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 "
+                                   "(the step would shard by whole matrices across GPUs; no multi-GPU path "
+                                   "is implemented)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
