@@ -172,3 +172,39 @@ def test_dion_host_validation_without_gpu(lib):
     assert call(q=P + 4) == mm.MUON_ERR_UNSUPPORTED          # misaligned
     assert call() == mm.MUON_ERR_WORKSPACE
     assert call(ws=P, wsz=lib.dion_workspace_size(2, 64, 96, 16) - 1) == mm.MUON_ERR_WORKSPACE
+
+
+def test_workspace_layout_properties(lib):
+    """For random group sets (every path: single-workgroup, thin, tiled; wide,
+    tall and square; any batch), the regions the layout query names lie inside
+    the workspace, are 256-byte aligned, hold every matrix of their group, and
+    the O regions of different groups do not overlap (host logic only)."""
+    import random
+    import matrix_orthogonalizing_optimizer_muon_amd as mm
+    rng = random.Random(1234)
+    sides = [1, 7, 33, 96, 97, 128, 200, 256, 300, 512, 777, 1024, 2100]
+    for _ in range(300):
+        n = rng.randint(1, mm.MAX_GROUPS)
+        g = (mm._Group * n)()
+        shapes = []
+        for k in range(n):
+            r, c, b = rng.choice(sides), rng.choice(sides), rng.randint(1, 5)
+            g[k] = mm._Group(16, 16, 16, b, r, c, 0, r * c + rng.choice([0, 8]))
+            shapes.append((b, r, c))
+        total = lib.muon_step_workspace_size(g, n)
+        assert total > 0
+        steps = rng.choice([1, 5])
+        o_regions = []
+        for k, (b, r, c) in enumerate(shapes):
+            lay = mm._WsLayout()
+            assert lib.muon_step_workspace_layout(g, n, k, steps, ctypes.byref(lay)) == mm.MUON_OK
+            assert lay.o_offset % 256 == 0 and lay.inv_norm_offset % 256 == 0 and lay.x0_offset % 256 == 0
+            o_end = lay.o_offset + 2 * ((b - 1) * lay.o_batch_stride + (r - 1) * lay.o_ld + c)
+            assert lay.o_ld >= c and lay.o_batch_stride >= r * lay.o_ld and o_end <= total
+            assert lay.inv_norm_offset + 4 * b <= total
+            m, w = min(r, c), max(r, c)
+            assert lay.x0_ld >= w and lay.x0_offset + 2 * ((b - 1) * lay.x0_batch_stride + (m - 1) * lay.x0_ld + w) <= total
+            o_regions.append((lay.o_offset, o_end))
+        o_regions.sort()
+        for (a0, a1), (b0, b1) in zip(o_regions, o_regions[1:]):
+            assert a1 <= b0, (a0, a1, b0, b1)
