@@ -1,8 +1,10 @@
 """HIP graph capture of the path: the library launches only kernels on the
 caller's stream (no allocation, no memset, no synchronisation), so a whole
-MuonClip step can be captured once and replayed.  Each replay is checked
-bit for bit against the same number of eager steps on identical inputs,
-with eager work and synchronisations between the replays."""
+MuonClip step, and the companion entry points (the allocation-free S_max
+pass, the attention forward, AdamW, Dion), can be captured once and
+replayed.  Each replay is checked bit for bit against the same number of
+eager calls on identical inputs, with eager work and synchronisations
+between the replays."""
 import math
 import sys
 
@@ -98,3 +100,81 @@ def test_captured_step_replays_match_eager(mm):
         assert torch.equal(eager_flags, graph_flags)
         say(f"   replay {rep}: identical; flags {graph_flags.tolist()}")
     assert graph_flags.tolist()[1] == 1
+
+
+def test_captured_companions_replay_match_eager(mm):
+    """The other entry points under capture: the allocation-free S_max pass
+    (its partials in the library's own scratch), the attention forward with
+    its S_max export, a multi-tensor AdamW step and a Dion step, captured once
+    and replayed 3 times, each replay bit-identical to the same eager calls,
+    with eager work and synchronisations between the replays."""
+    import torch
+    dev = torch.device("cuda:0")
+    say("[graph] capture S_max (no-alloc), attention, AdamW and Dion, replay 3 times")
+    g = gen.rng(31)
+
+    def state():
+        Q = to_dev(gen.f32_to_bf16_bits(gen.gaussian(g, (2, 300, 3, 128), 1.0)), dev)
+        K = to_dev(gen.f32_to_bf16_bits(gen.gaussian(g, (2, 300, 3, 128), 1.0)), dev)
+        V = to_dev(gen.f32_to_bf16_bits(gen.gaussian(g, (2, 300, 3, 128), 1.0)), dev)
+        ps = [to_dev(gen.f32_to_bf16_bits(gen.gaussian(g, (n,), 0.02)), dev) for n in (1000, 4097, 64)]
+        gs = [to_dev(gen.f32_to_bf16_bits(gen.gaussian(g, (p.numel(),), 1.0)), dev) for p in ps]
+        ms = [torch.zeros(p.numel(), dtype=torch.float32, device=dev) for p in ps]
+        vs = [torch.zeros(p.numel(), dtype=torch.float32, device=dev) for p in ps]
+        W = to_dev(gen.f32_to_bf16_bits(gen.gaussian(g, (2, 256, 192), 0.02)), dev)
+        G = to_dev(gen.f32_to_bf16_bits(gen.gaussian(g, (2, 256, 192), 1.0)), dev)
+        M = torch.zeros((2, 256, 192), dtype=torch.float32, device=dev)
+        R = gen.gaussian(g, (2, 192, 16), 1.0)
+        R /= np.linalg.norm(R, axis=1, keepdims=True)
+        Qd = to_dev(R.astype(np.float32), dev)
+        return [Q, K, V, ps, gs, ms, vs, W, G, M, Qd]
+
+    first = state()
+    eager = [t.clone() if not isinstance(t, list) else [x.clone() for x in t] for t in first]
+    static = first
+
+    def make(st):
+        Q, K, V, ps, gs, ms, vs, W, G, M, Qd = st
+        s_a = torch.empty(3, dtype=torch.float32, device=dev)
+        s_b = torch.empty(3, dtype=torch.float32, device=dev)
+        out = torch.empty_like(Q)
+        aws = torch.empty(max(mm.load_library().attn_fwd_workspace_size(2, 300, 3), 256), dtype=torch.uint8,
+                          device=dev)
+        dws = torch.empty(max(mm.load_library().dion_workspace_size(2, 256, 192, 16), 256), dtype=torch.uint8,
+                          device=dev)
+
+        def step():
+            mm.qkclip_rowmax_noalloc(Q, K, 1.0 / math.sqrt(128), True, out=s_a)
+            mm.attn_fwd(Q, K, V, 1.0 / math.sqrt(128), True, out=out, s_max=s_b, workspace=aws)
+            mm.adamw_step(ps, gs, ms, vs, lr=1e-3, step=1)
+            mm.dion_step(W, G, M, Qd, lr=0.01, workspace=dws)
+        return step, [s_a, s_b, out]
+
+    eager_step, eager_out = make(eager)
+    graph_step, graph_out = make(static)
+    # one eager call of every entry point on a third state first, so that
+    # nothing is done for the first time inside the capture
+    make(state())[0]()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        graph_step()
+    torch.cuda.synchronize()
+
+    def flat(st):
+        return [x for t in st for x in (t if isinstance(t, list) else [t])]
+
+    x = torch.randn(512, 512, device=dev)
+    for rep in range(3):
+        eager_step()
+        _ = x @ x                      # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t_e, t_s) in enumerate(zip(flat(eager) + eager_out, flat(static) + graph_out)):
+            assert torch.equal(t_e, t_s), f"replay {rep}: buffer {i} differs"
+        say(f"   replay {rep}: identical; s_max {graph_out[0].tolist()}")
+    # the two statistics agree
+    assert torch.allclose(graph_out[0], graph_out[1], rtol=1e-6, atol=0)
