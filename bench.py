@@ -860,8 +860,10 @@ def short_name(kernel):
 
 def summarize_profile(paths):
     """Per-kernel summary of rocprofv3 CSV output: a kernel trace
-    (*_kernel_trace.csv: calls and average / min / max duration) or a counter
-    collection (*_counter_collection.csv: mean counter value per dispatch)."""
+    (*_kernel_trace.csv: calls and average / min / max duration), a counter
+    collection (*_counter_collection.csv: mean counter value per dispatch) or
+    a marker trace (*_marker_api_trace.csv: the library's named host ranges,
+    calls and average / min / max host time)."""
     import csv
     from collections import defaultdict
     for path in paths:
@@ -869,7 +871,18 @@ def summarize_profile(paths):
         if not rows:
             continue
         print(f"# {os.path.basename(path)}")
-        if "Start_Timestamp" in rows[0]:
+        if "Function" in rows[0] and "Kernel_Name" not in rows[0]:
+            d = defaultdict(list)
+            order = []
+            for r in rows:
+                if r["Function"] not in d:
+                    order.append(r["Function"])
+                d[r["Function"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            print(f"# {'range':40s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+            for k in order:
+                v = d[k]
+                print(f"  {k:40s} {len(v):7d} {sum(v) / len(v):10.1f} {min(v):10.1f} {max(v):10.1f}")
+        elif "Start_Timestamp" in rows[0]:
             d = defaultdict(list)
             for r in rows:
                 d[short_name(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)

@@ -36,6 +36,9 @@
  *   - Calls on different streams are safe if their workspaces and outputs
  *     do not overlap.  The optional profiler (muon_profile_*) is process-wide
  *     and not thread-safe.
+ *   - Every entry point that launches work opens a named roctx range (and
+ *     muon_step one per stage), visible to rocprofv3 --marker-trace; the
+ *     library links librocprofiler-sdk-roctx for them.
  */
 #ifndef MUON_H
 #define MUON_H

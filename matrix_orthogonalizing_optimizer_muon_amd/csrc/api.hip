@@ -8,9 +8,22 @@
 #include <cmath>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "common.hpp"
 
 namespace muon {
+
+// Named host ranges (roctx) around each entry point and the Muon step's
+// stages, for `rocprofv3 --marker-trace`; near free when no tool is attached.
+namespace {
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
+}  // namespace
 
 // ----------------------------------------------------------------------------
 // optional event profiler
@@ -513,6 +526,7 @@ int muon_step(const muon_group_t* groups, int n_groups, int param_dtype, const m
   size_t need = 0;
   std::vector<Plan> plans = plans_for(groups, n_groups, need);
   if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
+  Range range("muon_step");
 
   const int fin = hp->ns_steps & 1;
   // small groups: the whole step in one launch, one workgroup per matrix,
@@ -571,12 +585,19 @@ int muon_step(const muon_group_t* groups, int n_groups, int param_dtype, const m
     bp.push_back(plans[g]);
     ins.push_back({groups[g].grad, groups[g].momentum});
   }
-  st = launch_prep(bp, ins, param_dtype, hp->momentum, hp->nesterov ? 1 : 0, workspace, stream);
-  if (st != MUON_OK) return st;
-  st = launch_finalize(bp, hp->ns_eps, workspace, stream);
-  if (st != MUON_OK) return st;
-  st = run_ns(bp, hp->ns_steps, hp->ns_a, hp->ns_b, hp->ns_c, workspace, nullptr, stream);
-  if (st != MUON_OK) return st;
+  {
+    Range stage("muon_step: momentum and normalisation");
+    st = launch_prep(bp, ins, param_dtype, hp->momentum, hp->nesterov ? 1 : 0, workspace, stream);
+    if (st != MUON_OK) return st;
+    st = launch_finalize(bp, hp->ns_eps, workspace, stream);
+    if (st != MUON_OK) return st;
+  }
+  {
+    Range stage("muon_step: Newton-Schulz");
+    st = run_ns(bp, hp->ns_steps, hp->ns_a, hp->ns_b, hp->ns_c, workspace, nullptr, stream);
+    if (st != MUON_OK) return st;
+  }
+  Range stage("muon_step: update");
 
   UpdateLaunch U{};
   U.ngroups = static_cast<int>(big.size());
@@ -626,6 +647,7 @@ int ns_orthogonalize(const void* in, int in_dtype, uint16_t* out, int batch, int
   std::vector<Plan> plans;
   plans.push_back(make_plan(batch, rows, cols, batch_stride, need));
   if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
+  Range range("ns_orthogonalize");
   if (small_ok(rows, cols)) {
     const Plan& p = plans[0];
     SmallLaunch S{};
@@ -697,6 +719,7 @@ int qkclip_rowmax(const uint16_t* Q, const uint16_t* K, int B, int T, int H, int
   if (st != MUON_OK) return st;
   const size_t need = qkclip_rowmax_workspace_size(B, T, H);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return MUON_ERR_WORKSPACE;
+  Range range("qkclip_rowmax");
   float* partial = static_cast<float*>(workspace);
   MUON_LAUNCH(KIND_QK_ROWMAX, stream,
               launch_qk_rowmax(reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K), B, T, H,
@@ -713,6 +736,7 @@ int qkclip_rowmax_noalloc(const uint16_t* Q, const uint16_t* K, int B, int T, in
   const int st = rowmax_args(Q, K, B, T, H, d_head, logit_scale, s_max, &nqb);
   if (st != MUON_OK) return st;
   if (static_cast<int64_t>(B) * H * nqb > kNoAllocPartials) return MUON_ERR_WORKSPACE;
+  Range range("qkclip_rowmax_noalloc");
   float* partial = nullptr;
   if (noalloc_partials(&partial) != hipSuccess) return MUON_ERR_HIP;
   // every partial the reduction reads is written by its row-max block first,
@@ -746,6 +770,7 @@ int qkclip_rescale_slices(const qkclip_slice_t* slices, int n_slices, int dtype,
     R.expo = q.exponent;
     R.vec = (q.cols % 8 == 0) && aligned(q.w, 16);
   }
+  Range range("qkclip_rescale");
   MUON_LAUNCH(KIND_QK_RESCALE, stream, launch_qk_rescale(L, dtype, H, s_max, tau, clipped, stream));
   return MUON_OK;
 }
@@ -782,6 +807,7 @@ int adamw_step(const adamw_tensor_t* tensors, int n_tensors, int dtype, const ad
                         !aligned(t.exp_avg_sq, 4)))
       return MUON_ERR_INVALID_ARG;
   }
+  Range range("adamw_step");
   AdamWLaunch A{};
   A.lr = hp->lr;
   A.beta1 = hp->beta1;
@@ -836,6 +862,7 @@ int attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int
   if (static_cast<int64_t>(B) * H * nqb > (int64_t(1) << 31) - 1) return MUON_ERR_INVALID_ARG;
   const size_t need = attn_fwd_workspace_size(B, T, H);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return MUON_ERR_WORKSPACE;
+  Range range("attn_fwd");
   AttnArgs A{};
   A.Q = reinterpret_cast<const bf16_t*>(Q);
   A.K = reinterpret_cast<const bf16_t*>(K);
@@ -915,6 +942,7 @@ int dion_step(void* param, int dtype, const void* grad, float* momentum, float* 
   const DionPlan d = dion_plan(batch, rows, cols, rank);
   if (!workspace || workspace_bytes < d.total || !aligned(workspace, kAlign)) return MUON_ERR_WORKSPACE;
 
+  Range range("dion_step");
   DionArgs A{};
   A.G = grad;
   A.M = momentum;
