@@ -91,6 +91,31 @@ def test_ns_orthogonalize_matches_oracle(mm, dev, shape, dtype):
         assert err <= ns_tolerance(r, c)
 
 
+# Other step counts through ns_orthogonalize: an even count (the result then
+# comes from the other ping-pong buffer) on every path (tiled with both tile
+# sizes, thin, single-workgroup), and the limit of 64 steps with the textbook
+# cubic (1.5, -0.5, 0), which by then has taken every singular value to 1:
+# the result is the polar factor U V^T (the oracle's iteration, checked
+# against numpy's SVD in tests/test_oracle_ns.py) within the same tolerance.
+@pytest.mark.parametrize("shape,steps,coeffs", [
+    ((300, 600), 4, (3.4445, -4.7750, 2.0315)), ((640, 520), 2, (3.4445, -4.7750, 2.0315)),
+    ((33, 777), 4, (3.4445, -4.7750, 2.0315)), ((96, 160), 4, (3.4445, -4.7750, 2.0315)),
+    ((200, 520), 64, (1.5, -0.5, 0.0)), ((700, 300), 64, (1.5, -0.5, 0.0)), ((777, 33), 64, (1.5, -0.5, 0.0))])
+def test_ns_other_step_counts(mm, dev, shape, steps, coeffs):
+    import torch
+    say(f"[ns steps] shape={shape} steps={steps} coeffs={coeffs}")
+    r, c = shape
+    g = gen.rng(r * 7 + c + steps)
+    X = gen.f32_to_bf16_bits(gen.gaussian(g, (1, r, c), 1.0))
+    out = mm.ns_orthogonalize(to_dev(X, dev), steps=steps, coeffs=coeffs)
+    torch.cuda.synchronize()
+    got = O.bf16_bits_to_f64(to_host(out))[0]
+    ref = O.newton_schulz(O.bf16_bits_to_f64(X[0]), steps, *coeffs)
+    err = rel_fro(got, ref)
+    say(f"   rel err {err:.3e}")
+    assert err <= ns_tolerance(r, c)
+
+
 # Batches whose symmetric products (X X^T and the polynomial) leave a last
 # wave at most half full on the chip: those last 256-tiles run as 256 x 128
 # column halves in a second launch.
@@ -218,7 +243,7 @@ def check_step(mm, wl, host, devg, ws, hp, sample=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("ns_steps", [5, 1])
+@pytest.mark.parametrize("ns_steps", [5, 2, 1])
 def test_muon_step_stages_ragged(mm, dev, dtype, ns_steps):
     """All stages of one step on four ragged groups (two tile sizes, tall and
     wide); with ns_steps == 1 the workspace still holds X0 = bf16(U)."""
@@ -261,7 +286,7 @@ THIN_SHAPES = ((33, 777), (777, 33), (1, 300), (300, 1), (96, 1000), (64, 2100))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("ns_steps", [5, 1])
+@pytest.mark.parametrize("ns_steps", [5, 4, 1])
 def test_muon_step_thin_groups(mm, dev, dtype, ns_steps):
     """Every stage of one step for thin groups, all in one call next to a
     tiled group; with ns_steps == 1 the workspace still holds X0."""
