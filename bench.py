@@ -192,10 +192,10 @@ def main():
     if out_sigma:
         out["ns_sigma_band"] = out_sigma
     torch.cuda.empty_cache()
-    hbm = None if args.headline_only else hbm_ceiling(mm, torch, dev)
+    hbm = None if args.headline_only else hbm_stream_rates(mm, torch, dev)
     if hbm:
-        out["hbm_measured_ceiling"] = hbm
-        attach_hbm_ceiling(out["hbm_passes"], hbm)
+        out["hbm_stream_probe"] = hbm
+        attach_hbm_probe(out["hbm_passes"], hbm)
         note(f"HBM stream probe: {hbm['mix_6r_8w_GBs']} GB/s for the momentum pass's mix, "
              f"{hbm['mix_4r_2w_GBs']} for the update's, {hbm['copy_GBs']} for a copy")
 
@@ -203,7 +203,7 @@ def main():
         out["muonclip_layer"] = muonclip_layer_reading(mm, torch, dev, seed, args.steps, args.warmup,
                                                        companions=True)
         if hbm:
-            attach_hbm_ceiling(out["muonclip_layer"]["hbm_passes"], hbm)
+            attach_hbm_probe(out["muonclip_layer"]["hbm_passes"], hbm)
         note("MuonClip layer step timed")
         out["layer_hidden2048"] = muon_config_run(mm, torch, dev, seed, 2, args.steps, args.warmup)
         note("hidden-2048 layer timed")
@@ -255,7 +255,7 @@ def mfma_peak(mm, torch, dev, iters=8000):
                      "register operands (smooth operands beside it), best of 3 after ~80 ms of warm-up"}
 
 
-def hbm_ceiling(mm, torch, dev, gib=3):
+def hbm_stream_rates(mm, torch, dev, gib=3):
     """The HBM stream probe (muon_hbm_probe) on `gib` GiB streams for the
     read/write mixes of the two passes and a plain copy: 6 B read and 8 B
     written per element (the momentum pass with its transposed X0 copy),
@@ -288,11 +288,11 @@ def hbm_ceiling(mm, torch, dev, gib=3):
     return res
 
 
-def attach_hbm_ceiling(passes, hbm):
+def attach_hbm_probe(passes, hbm):
     """Each HBM pass's moved bytes against the probe's rate for its mix."""
     for k, key in (("momentum_norm", "mix_6r_8w_GBs"), ("param_update", "mix_4r_2w_GBs")):
         if k in passes and hbm.get(key):
-            passes[k]["frac_of_measured_ceiling"] = round(passes[k]["GBs_moved"] / hbm[key], 4)
+            passes[k]["frac_of_stream_probe"] = round(passes[k]["GBs_moved"] / hbm[key], 4)
 
 
 def make_config_groups(mm, torch, dev, seed, idx):

@@ -70,8 +70,8 @@ def test_hbm_pass_bytes():
     assert mom["GBs"] == pytest.approx(12 * elem / 500e-6 / 1e9)
     assert mom["frac"] == pytest.approx(mom["GBs"] / 8000.0, abs=1e-4)
     assert mom["traffic"] is None
-    bench.attach_hbm_ceiling(out, {"mix_6r_8w_GBs": mom["GBs_moved"] * 2, "mix_4r_2w_GBs": upd["GBs_moved"]})
-    assert mom["frac_of_measured_ceiling"] == 0.5 and upd["frac_of_measured_ceiling"] == 1.0
+    bench.attach_hbm_probe(out, {"mix_6r_8w_GBs": mom["GBs_moved"] * 2, "mix_4r_2w_GBs": upd["GBs_moved"]})
+    assert mom["frac_of_stream_probe"] == 0.5 and upd["frac_of_stream_probe"] == 1.0
 
 
 def write_csv(path, rows):
