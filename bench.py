@@ -50,6 +50,9 @@ def parse():
                     help="time the decoder step alone (for profiler runs)")
     ap.add_argument("--layer-only", action="store_true",
                     help="time the MuonClip layer step alone (for profiler runs)")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time the attention forward with its S_max export alone, at the MuonClip "
+                         "layer's shape (for profiler runs)")
     ap.add_argument("--seed", type=int, default=5000)
     ap.add_argument("--blas-reference", action="store_true",
                     help="time torch.matmul (hipBLASLt) on the full, unsymmetric Newton-Schulz "
@@ -154,6 +157,15 @@ def main():
     if args.layer_only:
         res = muonclip_layer_reading(mm, torch, dev, seed, args.steps, args.warmup)
         print(json.dumps(res), flush=True)
+        return
+    if args.attention_only:
+        from synthetic import generators as gen
+        B, T, H, D = 4, 4096, 64, 128
+        Q = gen.bulk_normal_torch((B, T, H, D), 1.0, seed + 41, dev, torch.bfloat16)
+        K = gen.bulk_normal_torch((B, T, H, D), 1.0, seed + 42, dev, torch.bfloat16)
+        res = attention_companion(mm, torch, dev, seed, Q, K, B, T, H, D, (0.0, 0), reps=args.steps)
+        print(json.dumps({"workload": f"attention forward with S_max, B {B} x T {T} x H {H} x d {D}, causal",
+                          **res}), flush=True)
         return
 
     # ---------------- headline: the 24-layer decoder's Muon group
